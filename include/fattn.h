@@ -1,0 +1,114 @@
+/*
+ * libfattn — exact scaled-dot-product attention computed tile by tile (FlashAttention style)
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (page "FlashAttention为什么更快更省显存", opening formula; page
+ * "从零实现 FlashAttention-2：分块在线 Softmax", sections on the rescale identity and on the
+ * backward): for every batch b and head h, with S = scale * Q K^T,
+ *
+ *     O   = softmax(S) V          (row-wise softmax; S[i][j] = -inf for j > i when causal)
+ *     LSE = log(sum_j exp(S[i][j]))   per query row, natural log, float32
+ *
+ * The forward never materialises S or P: it keeps a query tile on chip, streams key/value tiles
+ * past it and merges each tile into a running row max, exp-sum and unnormalised output (page
+ * "mianstack q-0277", section on keeping the blockwise softmax normalised). The backward rebuilds
+ * the probability tiles from Q, K, V and the saved LSE instead of storing them (page 2, backward
+ * section; page 1, section on why the backward recomputes).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense, contiguous [B, H, N, d] with d innermost, in the element type `dtype`.
+ *    LSE (and the workspace's D vector) is float32 [B, H, N].
+ *  - Every pointer is a caller-owned DEVICE pointer on the current HIP device, 16-byte aligned.
+ *    The library allocates nothing, keeps no global mutable state and is re-entrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream). Work is enqueued
+ *    on it and the call returns at once; the caller synchronises.
+ *  - Arguments are checked on the host before any HIP call: a call that returns an error has
+ *    enqueued nothing and written nothing. The library never aborts or throws across this ABI.
+ *    A launch failure returns FATTN_ERR_LAUNCH; faults inside a kernel surface at the caller's
+ *    synchronisation.
+ *  - Outputs must not overlap inputs (an exact pointer match is rejected with FATTN_ERR_ALIAS;
+ *    partial overlap is undefined behaviour).
+ *  - Supported: d in {64, 128}; 1 <= N <= 16777216; B, H >= 1 with B*H*N*d < 2^46; `scale`
+ *    finite (0 gives uniform attention, negative values are allowed); causal in {0, 1}.
+ *    Causal masks key j > query i (queries and keys share the same length N).
+ */
+#ifndef FATTN_H
+#define FATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FATTN_F32 = 0, FATTN_F16 = 1, FATTN_BF16 = 2 } fattn_dtype;
+
+typedef enum {
+  FATTN_OK = 0,
+  FATTN_ERR_NULL = -1,        /* a required pointer is NULL */
+  FATTN_ERR_SHAPE = -2,       /* B, H or N out of range, or the sizes overflow */
+  FATTN_ERR_HEADDIM = -3,     /* d not in {64, 128} */
+  FATTN_ERR_DTYPE = -4,       /* unknown dtype, or a dtype this entry point does not support */
+  FATTN_ERR_TILE = -5,        /* (Br, Bc) not a supported tile shape for this dtype and d */
+  FATTN_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned */
+  FATTN_ERR_SCALE = -7,       /* scale is NaN or infinite */
+  FATTN_ERR_WORKSPACE = -8,   /* workspace NULL or smaller than fattn_bwd_workspace_size() */
+  FATTN_ERR_UNSUPPORTED = -9, /* a valid request this build does not implement */
+  FATTN_ERR_LAUNCH = -10,     /* the HIP runtime rejected a kernel launch */
+  FATTN_ERR_ALIAS = -11,      /* an output pointer equals an input pointer */
+  FATTN_ERR_CAUSAL = -12      /* causal not 0 or 1 */
+} fattn_status;
+
+/*
+ * Forward pass. Reads q, k, v [B,H,N,d] (dtype); writes o [B,H,N,d] (dtype, round-to-nearest-
+ * even from the float32 accumulator) and lse [B,H,N] (float32, natural log of the row's exp-sum
+ * of scaled logits). Picks the tile shape for (dtype, d, causal) itself.
+ * Computation: page 2, hands-on section (query tiles outer, key/value tiles inner, causal mask
+ * inside the tile loop); page 3's merge rule for the running statistics; final division by the
+ * exp-sum after the last tile (page 2, rescale-identity section).
+ */
+int fattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fattn_fwd with an explicit tile shape: Br query rows per work-group, Bc key rows per step
+ * (page 2, tips: the tile sizes change the on-chip working set, not the result). Br = Bc = 0
+ * selects the default, so fattn_fwd(...) == fattn_fwd_tiled(..., 0, 0, stream).
+ * Supported (Br, Bc): f16/bf16 — {64, 128} x {64, 128}; f32 — (128, 32) and (64, 32).
+ */
+int fattn_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N, int d, float scale, int causal, int dtype,
+                    int Br, int Bc, void* stream);
+
+/*
+ * Bytes of device workspace fattn_bwd needs: the float32 row vector D = rowsum(dO * O)
+ * [B,H,N] plus the float32 dQ accumulator [B,H,N,d]. Returns 0 for arguments that fattn_bwd would
+ * reject on shape, head dim or dtype grounds.
+ */
+size_t fattn_bwd_workspace_size(int B, int H, int N, int d, int dtype);
+
+/*
+ * Backward pass by recomputation (page 2, backward section; page 3, backward section).
+ * Reads q, k, v, o, dO [B,H,N,d] (dtype) and lse [B,H,N] (float32, as written by fattn_fwd);
+ * writes dq, dk, dv [B,H,N,d] (dtype, from float32 accumulators). P is rebuilt tile by tile as
+ * exp(S - LSE) and never stored. `workspace` is caller-owned device memory of at least
+ * fattn_bwd_workspace_size() bytes; its contents on entry are ignored and on exit unspecified.
+ * dtype: FATTN_F16 or FATTN_BF16 (FATTN_F32 returns FATTN_ERR_DTYPE).
+ */
+int fattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+              const float* lse, void* dq, void* dk, void* dv,
+              int B, int H, int N, int d, float scale, int causal, int dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fattn_strerror(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FATTN_H */

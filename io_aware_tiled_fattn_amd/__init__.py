@@ -1,0 +1,165 @@
+"""Python binding of libfattn (exact FlashAttention-style attention for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels behind the
+C ABI declared in include/fattn.h. PyTorch is used to allocate device memory and to name the
+stream; there is no CPU or PyTorch fallback, and a missing library raises.
+
+Low-level names mirror the C entry points (``fattn_fwd``, ``fattn_fwd_tiled``, ``fattn_bwd``,
+``fattn_bwd_workspace_size``, ``fattn_strerror``, ``fattn_version``) and take raw device
+addresses. ``forward`` and ``backward`` wrap them for contiguous [B, H, N, d] torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FATTN_F32", "FATTN_F16", "FATTN_BF16", "FattnError", "lib", "library_path",
+    "fattn_fwd", "fattn_fwd_tiled", "fattn_bwd", "fattn_bwd_workspace_size", "fattn_strerror",
+    "fattn_version", "forward", "backward", "dtype_code",
+]
+
+FATTN_F32, FATTN_F16, FATTN_BF16 = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libfattn.so")
+
+
+class FattnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fattn_strerror(status)} (status {status})")
+
+
+def lib():
+    """Load libfattn.so (built in-tree by io_aware_tiled_fattn_amd.build); raise if missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libfattn.so not found at {path}; build it with "
+                           "`python -m io_aware_tiled_fattn_amd.build` (no fallback exists)")
+    L = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.fattn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    L.fattn_fwd.restype = i
+    L.fattn_fwd_tiled.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i, vp]
+    L.fattn_fwd_tiled.restype = i
+    L.fattn_bwd_workspace_size.argtypes = [i, i, i, i, i]
+    L.fattn_bwd_workspace_size.restype = sz
+    L.fattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
+    L.fattn_bwd.restype = i
+    L.fattn_strerror.argtypes = [i]
+    L.fattn_strerror.restype = ctypes.c_char_p
+    L.fattn_version.argtypes = []
+    L.fattn_version.restype = i
+    _LIB = L
+    return L
+
+
+# --- raw C-ABI mirrors (pointers are ints: device addresses; stream is an int or None) -------
+
+
+def fattn_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream=None) -> int:
+    return lib().fattn_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream)
+
+
+def fattn_fwd_tiled(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, Br, Bc, stream=None) -> int:
+    return lib().fattn_fwd_tiled(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, Br, Bc, stream)
+
+
+def fattn_bwd_workspace_size(B, H, N, d, dtype) -> int:
+    return lib().fattn_bwd_workspace_size(B, H, N, d, dtype)
+
+
+def fattn_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype,
+              workspace, workspace_bytes, stream=None) -> int:
+    return lib().fattn_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype,
+                           workspace, workspace_bytes, stream)
+
+
+def fattn_strerror(status: int) -> str:
+    return lib().fattn_strerror(status).decode()
+
+
+def fattn_version() -> int:
+    return lib().fattn_version()
+
+
+# --- torch-tensor wrappers ---------------------------------------------------------------------
+
+
+def dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: FATTN_F32, torch.float16: FATTN_F16, torch.bfloat16: FATTN_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _check(t, name, like=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+    if like is not None and (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device):
+        raise ValueError(f"{name} must match q in shape, dtype and device")
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def forward(q, k, v, causal=False, scale=None, Br=0, Bc=0, out=None, lse=None, stream=None):
+    """O, LSE for contiguous [B, H, N, d] device tensors (float32, float16 or bfloat16).
+
+    ``out`` and ``lse`` may be given to write into existing tensors (no allocation then).
+    """
+    import torch
+    _check(q, "q")
+    _check(k, "k", q)
+    _check(v, "v", q)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(out, "out", q)
+    st = fattn_fwd_tiled(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         B, H, N, d, float(scale), int(bool(causal)), dtype_code(q), int(Br), int(Bc),
+                         _stream(stream))
+    if st != 0:
+        raise FattnError(st, "fattn_fwd")
+    return out, lse
+
+
+def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, stream=None):
+    """dQ, dK, dV for contiguous [B, H, N, d] float16/bfloat16 device tensors."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, q if n != "q" else None)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = dtype_code(q)
+    need = fattn_bwd_workspace_size(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = fattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                   lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                   B, H, N, d, float(scale), int(bool(causal)), code,
+                   workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != 0:
+        raise FattnError(st, "fattn_bwd")
+    return dq, dk, dv

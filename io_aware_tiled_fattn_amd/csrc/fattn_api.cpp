@@ -1,0 +1,123 @@
+// C-ABI entry points of libfattn: argument checks (host only, before any HIP call) and dispatch.
+#include "../../include/fattn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fattn_launch.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr long long kMaxN = 16777216LL;
+constexpr long long kMaxElems = 1LL << 46;
+
+int elem_bytes(int dtype) { return dtype == FATTN_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int B, int H, int N, int d, int dtype) {
+  if (dtype != FATTN_F32 && dtype != FATTN_F16 && dtype != FATTN_BF16) return FATTN_ERR_DTYPE;
+  if (d != 64 && d != 128) return FATTN_ERR_HEADDIM;
+  if (B < 1 || H < 1 || N < 1 || N > kMaxN) return FATTN_ERR_SHAPE;
+  const long long bh = (long long)B * H;
+  if (bh > (1LL << 31) - 1) return FATTN_ERR_SHAPE;
+  if (bh * N > kMaxElems / d) return FATTN_ERR_SHAPE;
+  // the forward grid is B*H*ceil(N/64) blocks at most; keep it in 32 bits
+  if (bh * ((N + 63) / 64) > 0x7fffffffLL) return FATTN_ERR_SHAPE;
+  return FATTN_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? FATTN_OK : FATTN_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int fattn_version(void) { return kVersion; }
+
+const char* fattn_strerror(int status) {
+  switch (status) {
+    case FATTN_OK: return "ok";
+    case FATTN_ERR_NULL: return "a required pointer is NULL";
+    case FATTN_ERR_SHAPE: return "B, H or N out of range";
+    case FATTN_ERR_HEADDIM: return "head dim d must be 64 or 128";
+    case FATTN_ERR_DTYPE: return "unsupported dtype for this entry point";
+    case FATTN_ERR_TILE: return "unsupported tile shape (Br, Bc)";
+    case FATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case FATTN_ERR_SCALE: return "scale is not finite";
+    case FATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case FATTN_ERR_UNSUPPORTED: return "not implemented in this build";
+    case FATTN_ERR_LAUNCH: return "kernel launch failed";
+    case FATTN_ERR_ALIAS: return "an output aliases an input";
+    case FATTN_ERR_CAUSAL: return "causal must be 0 or 1";
+    default: return "unknown status";
+  }
+}
+
+int fattn_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N, int d, float scale, int causal, int dtype,
+                    int Br, int Bc, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FATTN_ERR_NULL;
+  int st = check_common(B, H, N, d, dtype);
+  if (st != FATTN_OK) return st;
+  if (causal != 0 && causal != 1) return FATTN_ERR_CAUSAL;
+  if (!std::isfinite(scale)) return FATTN_ERR_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FATTN_ERR_ALIGN;
+  if (o == q || o == k || o == v || (const void*)lse == q || (const void*)lse == k ||
+      (const void*)lse == v || (void*)lse == o)
+    return FATTN_ERR_ALIAS;
+  if (Br == 0 && Bc == 0) {
+    if (!fattn::fwd_default_tile(dtype, d, causal, &Br, &Bc)) return FATTN_ERR_TILE;
+  } else if (!fattn::fwd_tile_supported(dtype, d, Br, Bc)) {
+    return FATTN_ERR_TILE;
+  }
+  fattn::FwdReq r{q, k, v, o, lse, B, H, N, d, scale, causal, dtype, Br, Bc};
+  (void)elem_bytes;
+  return launch_status(fattn::launch_fwd(r, (hipStream_t)stream));
+}
+
+int fattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int N, int d, float scale, int causal, int dtype, void* stream) {
+  return fattn_fwd_tiled(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, 0, 0, stream);
+}
+
+size_t fattn_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
+  if (check_common(B, H, N, d, dtype) != FATTN_OK) return 0;
+  if (dtype == FATTN_F32) return 0;
+  return fattn::bwd_workspace_bytes(B, H, N, d);
+}
+
+int fattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+              const float* lse, void* dq, void* dk, void* dv,
+              int B, int H, int N, int d, float scale, int causal, int dtype,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FATTN_ERR_NULL;
+  int st = check_common(B, H, N, d, dtype);
+  if (st != FATTN_OK) return st;
+  if (dtype == FATTN_F32) return FATTN_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FATTN_ERR_CAUSAL;
+  if (!std::isfinite(scale)) return FATTN_ERR_SCALE;
+  const void* ins[6] = {q, k, v, o, dO, lse};
+  void* outs[3] = {dq, dk, dv};
+  for (const void* p : ins)
+    if (!aligned16(p)) return FATTN_ERR_ALIGN;
+  for (void* p : outs)
+    if (!aligned16(p)) return FATTN_ERR_ALIGN;
+  for (void* p : outs)
+    for (const void* s : ins)
+      if (p == s) return FATTN_ERR_ALIAS;
+  if (dq == dk || dq == dv || dk == dv) return FATTN_ERR_ALIAS;
+  const size_t need = fattn::bwd_workspace_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < need) return FATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FATTN_ERR_ALIGN;
+  for (void* p : outs)
+    if (p == workspace) return FATTN_ERR_ALIAS;
+  for (const void* s : ins)
+    if (s == workspace) return FATTN_ERR_ALIAS;
+  fattn::BwdReq r{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, (float*)workspace};
+  return launch_status(fattn::launch_bwd(r, (hipStream_t)stream));
+}
+
+}  // extern "C"

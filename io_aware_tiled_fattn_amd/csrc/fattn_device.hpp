@@ -1,0 +1,93 @@
+// Device primitives for the gfx950 (CDNA4) attention kernels: element traits, MFMA wrappers,
+// the LDS transposed read, and the cross-half-wave reductions.
+//
+// Register layouts used throughout (v_mfma_f32_32x32x16_{bf16,f16}, wave64, lane l, h = l / 32):
+//   A operand (M x K = 32 x 16): lane l holds A[l % 32][8h + i], i = 0..7
+//   B operand (K x N = 16 x 32): lane l holds B[8h + i][l % 32]
+//   C/D (32 x 32, 16 floats)    : lane l holds D[8j + 4h + r][l % 32] in element 4j + r
+// The float32 path uses v_mfma_f32_32x32x2_f32: A[l % 32][h], B[h][l % 32], same C/D layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fattn {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element traits for the 16-bit input types: MFMA on 8-element fragments, RNE conversions.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+
+struct Bf16 {
+  using vec8 = bf16x8;
+  using scalar = __bf16;
+  static __device__ inline f32x16 mma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ inline scalar from_f32(float x) { return (__bf16)x; }
+  // two floats -> two RNE bf16 in one dword (low half = x)
+  static __device__ inline uint32_t pack2(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x, y}, bf16x2v));
+  }
+};
+struct F16 {
+  using vec8 = f16x8;
+  using scalar = _Float16;
+  static __device__ inline f32x16 mma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ inline scalar from_f32(float x) { return (_Float16)x; }
+  static __device__ inline uint32_t pack2(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x, y}, f16x2v));
+  }
+};
+
+template <typename V, typename U>
+__device__ inline V bitcast(U u) {
+  static_assert(sizeof(U) == sizeof(V), "bitcast size");
+  return __builtin_bit_cast(V, u);
+}
+
+// Cross-half reductions: lanes l and l ^ 32 combine (v_permlane32_swap gives both halves).
+__device__ inline float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j receives element j % 4 of the 8-byte
+// chunks addressed by lanes 4e + j / 4 (e = 0..3), i.e. a 4 x 16 block of 16-bit elements whose
+// four rows are addressed by lanes {0..3}, {4..7}, {8..11}, {12..15} (each lane one 4-element
+// quarter of its row) comes back column by column.
+__device__ inline i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+__device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// Block index remap so that consecutive logical blocks share an XCD: hardware dispatches block
+// ids round-robin over the 8 XCDs, so physical id x runs on XCD x % 8. When the grid is a
+// multiple of 8 the logical order visits, per XCD, one contiguous range of work.
+__device__ inline int xcd_remap(int bid, int nblocks) {
+  if ((nblocks & 7) != 0) return bid;
+  return (bid & 7) * (nblocks >> 3) + (bid >> 3);
+}
+
+}  // namespace fattn

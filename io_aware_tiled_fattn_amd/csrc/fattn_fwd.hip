@@ -1,0 +1,520 @@
+// Forward kernels: exact attention, one work-group per (batch*head, query tile).
+//
+// Method (page "从零实现 FlashAttention-2：分块在线 Softmax", FA-1 to FA-2 section and hands-on
+// section; page "mianstack q-0277", merge rule): a query tile stays on chip (in registers) while
+// the key/value tiles of its head stream through LDS. Each key tile updates, per query row, a
+// running max m, an exp-sum l and an unnormalised output accumulator; when the max grows the old
+// state is rescaled by exp(m_old - m_new). After the last tile O = acc / l and LSE = m + ln l.
+// Causal masking happens inside the tile loop; tiles wholly above the diagonal are never
+// visited (page 2, backward section and tips).
+//
+// gfx950 mapping (16-bit inputs):
+//  * a work-group of Br/32 waves; wave w owns query rows [q_base + 32w, +32).
+//  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: each lane then owns
+//    ONE query row (l % 32) and 16 keys per 32-key block, so the row max and row sum are
+//    in-register reductions plus one v_permlane32_swap between the two half-waves.
+//  * Q^T is the MFMA B operand, loaded once from HBM into registers; K is the A operand, read
+//    from a padded row-major LDS tile with ds_read_b128.
+//  * O^T = V^T P^T: P^T comes straight from the score accumulators (fp32 -> RNE 16-bit), V^T
+//    fragments come from the row-major V tile with ds_read_b64_tr_b16, so V is never transposed
+//    in memory. The MFMA reduction index is permuted consistently on both operands: slot s of
+//    half-wave h stands for key 16c + 4h + (s & 3) + 8 (s >> 2) of 16-key chunk c.
+//  * K/V tiles are double buffered in LDS; the next tile's global loads are issued before the
+//    current tile's math, one barrier per tile.
+//  * The running max is kept in the log2 domain with scale*log2(e) folded into one multiply, and
+//    is only moved when a row's max grows by more than kRescaleSlack (2^8): the factor is then
+//    exactly 1 for almost every tile (page 2, tips), the exp2 arguments stay <= 8, and the result
+//    is unchanged because O and l always share the same reference max.
+#include "fattn_device.hpp"
+#include "fattn_launch.hpp"
+
+#include "../../include/fattn.h"
+
+namespace fattn {
+namespace {
+
+constexpr float kRescaleSlack = 8.0f;
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int N;
+  int n_qtiles;
+  float c;            // |scale| * log2(e)
+  uint32_t neg_mask;  // 0x80008000 flips the sign of two packed 16-bit Q elements (scale < 0)
+};
+
+template <int D, int BR, int BC>
+struct FwdCfg {
+  static constexpr int NW = BR / 32;          // waves per work-group
+  static constexpr int NT = NW * 64;          // threads per work-group
+  static constexpr int KSTR = D + 8;          // K tile row pitch in LDS (elements)
+  static constexpr int VSTR = D + 16;         // V tile row pitch in LDS (elements)
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int CH = BC * CPR / NT;    // chunks per thread per tensor per tile
+  static constexpr int KBUF = BC * KSTR;
+  static constexpr int STAGE = KBUF + BC * VSTR;
+  static constexpr int LDS_ELEMS = 2 * STAGE;
+  static_assert(BC * CPR % NT == 0, "tile load split");
+  static_assert(BR % 32 == 0 && BC % 32 == 0 && D % 32 == 0, "tile shape");
+};
+
+template <typename TR, int D, int BR, int BC, bool CAUSAL>
+__global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
+  using Cfg = FwdCfg<D, BR, BC>;
+  using vec8 = typename TR::vec8;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[Cfg::LDS_ELEMS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int lr = lane & 31;
+  const int N = a.N;
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = logical / a.n_qtiles;
+  int qt = logical - bh * a.n_qtiles;
+  if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest rows first
+
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* __restrict__ Qh = a.q + head;
+  const uint16_t* __restrict__ Kh = a.k + head;
+  const uint16_t* __restrict__ Vh = a.v + head;
+
+  const int q_base = qt * BR;
+  const int q0 = q_base + 32 * w;
+  const int qrow = q0 + lr;
+  const bool wave_active = q0 < N;
+  const int wave_last = min(q0 + 31, N - 1);
+  const int wave_kv_end = CAUSAL ? wave_last + 1 : N;
+
+  // Q^T fragments: lane holds Q[qrow][16s + 8h .. +7].
+  vec8 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (qrow < N) raw = *(const u32x4*)(Qh + (size_t)qrow * D + 16 * s + 8 * h);
+    raw ^= a.neg_mask;
+    qf[s] = bitcast<vec8>(raw);
+  }
+
+  const int kv_end = CAUSAL ? min(N, q_base + BR) : N;
+  const int n_kv = (kv_end + BC - 1) / BC;
+
+  u32x4 kr[Cfg::CH], vr[Cfg::CH];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < Cfg::CH; ++i) {
+      const int c = tid + i * Cfg::NT;
+      const int row = c / Cfg::CPR;
+      const int col = c % Cfg::CPR;
+      const int key = j * BC + row;
+      if (key < N) {
+        kr[i] = *(const u32x4*)(Kh + (size_t)key * D + col * 8);
+        vr[i] = *(const u32x4*)(Vh + (size_t)key * D + col * 8);
+      } else {
+        kr[i] = u32x4{0u, 0u, 0u, 0u};
+        vr[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* Ks = smem + buf * Cfg::STAGE;
+    uint16_t* Vs = Ks + Cfg::KBUF;
+#pragma unroll
+    for (int i = 0; i < Cfg::CH; ++i) {
+      const int c = tid + i * Cfg::NT;
+      const int row = c / Cfg::CPR;
+      const int col = c % Cfg::CPR;
+      *(u32x4*)(Ks + row * Cfg::KSTR + col * 8) = kr[i];
+      *(u32x4*)(Vs + row * Cfg::VSTR + col * 8) = vr[i];
+    }
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
+  float m_ref = -__builtin_inff();
+  float l_part = 0.f;
+
+  load_tile(0);
+  store_tile(0);
+  for (int j = 0; j < n_kv; ++j) {
+    if (j + 1 < n_kv) load_tile(j + 1);
+    __syncthreads();
+    const int k0 = j * BC;
+    if (wave_active && k0 < wave_kv_end) {
+      const uint16_t* Ks = smem + (j & 1) * Cfg::STAGE;
+      const uint16_t* Vs = Ks + Cfg::KBUF;
+
+      // S^T = K Q^T for BC/32 blocks of 32 keys.
+      f32x16 s[BC / 32];
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+          const vec8 kf = *(const vec8*)(Ks + (kb * 32 + lr) * Cfg::KSTR + 16 * st + 8 * h);
+          s[kb] = TR::mma(kf, qf[st], s[kb]);
+        }
+      }
+
+      // Scale into the log2 domain, mask, row max.
+      const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float t = s[kb][e] * a.c;
+          if (need_mask) {
+            const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (key >= N || (CAUSAL && key > qrow)) t = -__builtin_inff();
+          }
+          s[kb][e] = t;
+          mx = fmaxf(mx, t);
+        }
+      mx = max_halves(mx);
+
+      // Move the reference max only when it grew by more than the slack.
+      const float m_new = fmaxf(m_ref, mx);
+      const bool grow = m_new > m_ref + kRescaleSlack;
+      if (wave_any(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+        if (grow) m_ref = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
+      }
+
+      // P^T = exp2(t - m_ref), packed to 16-bit MFMA B fragments (8 keys per 16-key chunk).
+      vec8 pf[BC / 16];
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          u32x4 packed;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float p0 = __builtin_amdgcn_exp2f(s[kb][8 * half + 2 * e2] - m_ref);
+            const float p1 = __builtin_amdgcn_exp2f(s[kb][8 * half + 2 * e2 + 1] - m_ref);
+            ls += p0 + p1;
+            packed[e2] = TR::pack2(p0, p1);
+          }
+          pf[2 * kb + half] = bitcast<vec8>(packed);
+        }
+      l_part += ls;
+
+      // O^T += V^T P^T; V^T fragments via the transposed LDS read.
+      const int tr_row = 4 * h + ((lane & 15) >> 2);
+      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+      for (int c = 0; c < BC / 16; ++c) {
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b) {
+          const uint16_t* p0 = Vs + (16 * c + tr_row) * Cfg::VSTR + 32 * b + tr_col;
+          const i16x4 lo = lds_read_tr16(p0);
+          const i16x4 hi = lds_read_tr16(p0 + 8 * Cfg::VSTR);
+          const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[b] = TR::mma(bitcast<vec8>(both), pf[c], acc[b]);
+        }
+      }
+    }
+    if (j + 1 < n_kv) store_tile((j + 1) & 1);
+  }
+
+  if (!wave_active) return;
+  const float l_tot = sum_halves(l_part);
+  if (qrow >= N) return;
+  const float inv = 1.0f / l_tot;
+  uint16_t* Orow = a.o + head + (size_t)qrow * D;
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      u32x2 v2;
+      v2[0] = TR::pack2(acc[b][4 * jj] * inv, acc[b][4 * jj + 1] * inv);
+      v2[1] = TR::pack2(acc[b][4 * jj + 2] * inv, acc[b][4 * jj + 3] * inv);
+      *(u32x2*)(Orow + 32 * b + 8 * jj + 4 * h) = v2;
+    }
+  if (h == 0) a.lse[(size_t)bh * N + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------------------------
+// float32 path: same algorithm on v_mfma_f32_32x32x2_f32 (full fp32 products), 32-key tiles.
+// The A operand of S^T is K[key][d = 2s + h], the B operand Q[query][2s + h]; for O^T the
+// reduction slot h of chunk (j, r) is key 8j + 4h + r, which is exactly where the score
+// accumulator already holds it, so P^T needs no repacking.
+
+template <int D, int BR>
+struct FwdCfgF32 {
+  static constexpr int BC = 32;
+  static constexpr int NW = BR / 32;
+  static constexpr int NT = NW * 64;
+  static constexpr int KSTR = D + 2;
+  static constexpr int VSTR = D + 4;
+  static constexpr int CPR = D / 4;  // 16-byte chunks per row
+  static constexpr int CH = BC * CPR / NT;
+  static constexpr int KBUF = BC * KSTR;
+  static constexpr int STAGE = KBUF + BC * VSTR;
+  static_assert(BC * CPR % NT == 0, "tile load split");
+};
+
+struct FwdArgsF32 {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  int N;
+  int n_qtiles;
+  float c;
+  float qsign;
+};
+
+template <int D, int BR, bool CAUSAL>
+__global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel_f32(FwdArgsF32 a) {
+  using Cfg = FwdCfgF32<D, BR>;
+  constexpr int BC = Cfg::BC;
+  __shared__ __attribute__((aligned(16))) float smem[2 * Cfg::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int lr = lane & 31;
+  const int N = a.N;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = logical / a.n_qtiles;
+  int qt = logical - bh * a.n_qtiles;
+  if (CAUSAL) qt = a.n_qtiles - 1 - qt;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const float* __restrict__ Qh = a.q + head;
+  const float* __restrict__ Kh = a.k + head;
+  const float* __restrict__ Vh = a.v + head;
+  const int q_base = qt * BR;
+  const int q0 = q_base + 32 * w;
+  const int qrow = q0 + lr;
+  const bool wave_active = q0 < N;
+  const int wave_kv_end = CAUSAL ? min(q0 + 31, N - 1) + 1 : N;
+
+  float qv[D / 2];
+#pragma unroll
+  for (int s = 0; s < D / 2; ++s) qv[s] = (qrow < N) ? Qh[(size_t)qrow * D + 2 * s + h] * a.qsign : 0.f;
+
+  const int kv_end = CAUSAL ? min(N, q_base + BR) : N;
+  const int n_kv = (kv_end + BC - 1) / BC;
+
+  f32x4 kr[Cfg::CH], vr[Cfg::CH];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < Cfg::CH; ++i) {
+      const int c = tid + i * Cfg::NT;
+      const int row = c / Cfg::CPR;
+      const int col = c % Cfg::CPR;
+      const int key = j * BC + row;
+      if (key < N) {
+        kr[i] = *(const f32x4*)(Kh + (size_t)key * D + col * 4);
+        vr[i] = *(const f32x4*)(Vh + (size_t)key * D + col * 4);
+      } else {
+        kr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        vr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    float* Ks = smem + buf * Cfg::STAGE;
+    float* Vs = Ks + Cfg::KBUF;
+#pragma unroll
+    for (int i = 0; i < Cfg::CH; ++i) {
+      const int c = tid + i * Cfg::NT;
+      const int row = c / Cfg::CPR;
+      const int col = c % Cfg::CPR;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ks[row * Cfg::KSTR + col * 4 + e] = kr[i][e];
+      *(f32x4*)(Vs + row * Cfg::VSTR + col * 4) = vr[i];
+    }
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
+  float m_ref = -__builtin_inff();
+  float l_part = 0.f;
+
+  load_tile(0);
+  store_tile(0);
+  for (int j = 0; j < n_kv; ++j) {
+    if (j + 1 < n_kv) load_tile(j + 1);
+    __syncthreads();
+    const int k0 = j * BC;
+    if (wave_active && k0 < wave_kv_end) {
+      const float* Ks = smem + (j & 1) * Cfg::STAGE;
+      const float* Vs = Ks + Cfg::KBUF;
+      f32x16 s;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+      for (int st = 0; st < D / 2; ++st)
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[lr * Cfg::KSTR + 2 * st + h], qv[st], s, 0, 0, 0);
+
+      const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float t = s[e] * a.c;
+        if (need_mask) {
+          const int key = k0 + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (key >= N || (CAUSAL && key > qrow)) t = -__builtin_inff();
+        }
+        s[e] = t;
+        mx = fmaxf(mx, t);
+      }
+      mx = max_halves(mx);
+      const float m_new = fmaxf(m_ref, mx);
+      const bool grow = m_new > m_ref + kRescaleSlack;
+      if (wave_any(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+        if (grow) m_ref = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
+      }
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s[e] = __builtin_amdgcn_exp2f(s[e] - m_ref);
+        ls += s[e];
+      }
+      l_part += ls;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = 8 * (e >> 2) + 4 * h + (e & 3);
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * Cfg::VSTR + 32 * b + lr], s[e], acc[b], 0, 0, 0);
+      }
+    }
+    if (j + 1 < n_kv) store_tile((j + 1) & 1);
+  }
+
+  if (!wave_active) return;
+  const float l_tot = sum_halves(l_part);
+  if (qrow >= N) return;
+  const float inv = 1.0f / l_tot;
+  float* Orow = a.o + head + (size_t)qrow * D;
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      f32x4 v4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v4[r] = acc[b][4 * jj + r] * inv;
+      *(f32x4*)(Orow + 32 * b + 8 * jj + 4 * h) = v4;
+    }
+  if (h == 0) a.lse[(size_t)bh * N + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Dispatch.
+
+template <typename TR, int D, int BR, int BC>
+hipError_t launch16(const FwdReq& r, hipStream_t st) {
+  FwdArgs a;
+  a.q = (const uint16_t*)r.q;
+  a.k = (const uint16_t*)r.k;
+  a.v = (const uint16_t*)r.v;
+  a.o = (uint16_t*)r.o;
+  a.lse = r.lse;
+  a.N = r.N;
+  a.n_qtiles = (r.N + BR - 1) / BR;
+  a.c = fabsf(r.scale) * kLog2e;
+  a.neg_mask = r.scale < 0.f ? 0x80008000u : 0u;
+  const long long nblk = (long long)r.B * r.H * a.n_qtiles;
+  const dim3 grid((unsigned)nblk), block(BR / 32 * 64);
+  if (r.causal)
+    hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, false>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D, int BR>
+hipError_t launch32(const FwdReq& r, hipStream_t st) {
+  FwdArgsF32 a;
+  a.q = (const float*)r.q;
+  a.k = (const float*)r.k;
+  a.v = (const float*)r.v;
+  a.o = (float*)r.o;
+  a.lse = r.lse;
+  a.N = r.N;
+  a.n_qtiles = (r.N + BR - 1) / BR;
+  a.c = fabsf(r.scale) * kLog2e;
+  a.qsign = r.scale < 0.f ? -1.f : 1.f;
+  const long long nblk = (long long)r.B * r.H * a.n_qtiles;
+  const dim3 grid((unsigned)nblk), block(BR / 32 * 64);
+  if (r.causal)
+    hipLaunchKernelGGL((fwd_kernel_f32<D, BR, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel_f32<D, BR, false>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename TR, int D>
+hipError_t launch16_tile(const FwdReq& r, hipStream_t st) {
+  if (r.Br == 128 && r.Bc == 64) return launch16<TR, D, 128, 64>(r, st);
+  if (r.Br == 128 && r.Bc == 128) return launch16<TR, D, 128, 128>(r, st);
+  if (r.Br == 64 && r.Bc == 64) return launch16<TR, D, 64, 64>(r, st);
+  if (r.Br == 64 && r.Bc == 128) return launch16<TR, D, 64, 128>(r, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool fwd_tile_supported(int dtype, int d, int Br, int Bc) {
+  if (d != 64 && d != 128) return false;
+  if (dtype == FATTN_F32) return Bc == 32 && (Br == 64 || Br == 128);
+  if (dtype == FATTN_F16 || dtype == FATTN_BF16) return (Br == 64 || Br == 128) && (Bc == 64 || Bc == 128);
+  return false;
+}
+
+bool fwd_default_tile(int dtype, int d, int causal, int* Br, int* Bc) {
+  (void)causal;
+  if (d != 64 && d != 128) return false;
+  if (dtype == FATTN_F32) {
+    *Br = 128;
+    *Bc = 32;
+    return true;
+  }
+  if (dtype == FATTN_F16 || dtype == FATTN_BF16) {
+    *Br = 128;
+    *Bc = 64;
+    return true;
+  }
+  return false;
+}
+
+hipError_t launch_fwd(const FwdReq& r, hipStream_t st) {
+  if (r.dtype == FATTN_F32) {
+    if (r.d == 64) return r.Br == 128 ? launch32<64, 128>(r, st) : launch32<64, 64>(r, st);
+    return r.Br == 128 ? launch32<128, 128>(r, st) : launch32<128, 64>(r, st);
+  }
+  if (r.dtype == FATTN_BF16) return r.d == 64 ? launch16_tile<Bf16, 64>(r, st) : launch16_tile<Bf16, 128>(r, st);
+  return r.d == 64 ? launch16_tile<F16, 64>(r, st) : launch16_tile<F16, 128>(r, st);
+}
+
+}  // namespace fattn

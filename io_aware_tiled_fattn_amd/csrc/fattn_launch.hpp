@@ -1,0 +1,48 @@
+// Internal interface between the C-ABI layer (argument checks, dispatch) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fattn {
+
+struct FwdReq {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, N, d;
+  float scale;
+  int causal;
+  int dtype;  // fattn_dtype
+  int Br, Bc; // resolved tile shape (never 0 here)
+};
+
+struct BwdReq {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, N, d;
+  float scale;
+  int causal;
+  int dtype;
+  float* dvec;  // workspace: D = rowsum(dO * O), float32 [B, H, N]
+};
+
+// Default forward tile for (dtype, d, causal): returns false if none exists.
+bool fwd_default_tile(int dtype, int d, int causal, int* Br, int* Bc);
+// Whether a forward kernel instance exists for this combination.
+bool fwd_tile_supported(int dtype, int d, int Br, int Bc);
+hipError_t launch_fwd(const FwdReq& r, hipStream_t stream);
+
+size_t bwd_workspace_bytes(int B, int H, int N, int d);
+hipError_t launch_bwd(const BwdReq& r, hipStream_t stream);
+
+}  // namespace fattn

@@ -1,0 +1,114 @@
+"""The C-ABI library loads without a GPU, exports every declared symbol, and rejects every bad
+argument on the host before any HIP call (so these calls are safe with fake device pointers)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import io_aware_tiled_fattn_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fattn.h")
+
+# Fake, 16-byte-aligned device addresses: only ever passed to calls that must fail validation.
+P = [0x10000 * (i + 1) for i in range(12)]
+MIS = 0x10008  # 8-byte aligned only
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fattn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fa.library_path()):
+        pytest.fail("libfattn.so is not built (run python -m io_aware_tiled_fattn_amd.build)")
+    return fa.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert {"fattn_fwd", "fattn_fwd_tiled", "fattn_bwd", "fattn_bwd_workspace_size",
+            "fattn_strerror", "fattn_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+        assert getattr(fa, n) is not None
+
+
+def test_version_and_strerror(L):
+    assert fa.fattn_version() >= 100
+    for code in range(0, -13, -1):
+        s = fa.fattn_strerror(code)
+        assert s and s != "unknown status", code
+    assert fa.fattn_strerror(12345) == "unknown status"
+
+
+def fwd(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=16, d=64, scale=0.125,
+             causal=0, dtype=fa.FATTN_BF16, Br=0, Bc=0, stream=None)
+    a.update(kw)
+    return fa.fattn_fwd_tiled(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                              a["d"], a["scale"], a["causal"], a["dtype"], a["Br"], a["Bc"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+    (dict(B=0), -2), (dict(H=0), -2), (dict(N=0), -2), (dict(N=-5), -2), (dict(B=-1), -2),
+    (dict(N=16777217), -2), (dict(B=65536, H=65536), -2),
+    (dict(d=96), -3), (dict(d=32), -3), (dict(d=256), -3), (dict(d=0), -3),
+    (dict(dtype=3), -4), (dict(dtype=-1), -4),
+    (dict(Br=96, Bc=64), -5), (dict(Br=128, Bc=32), -5), (dict(Br=64, Bc=0), -5),
+    (dict(dtype=fa.FATTN_F32, Br=128, Bc=64), -5),
+    (dict(q=MIS), -6), (dict(o=MIS), -6), (dict(lse=MIS), -6),
+    (dict(scale=float("nan")), -7), (dict(scale=float("inf")), -7), (dict(scale=-math.inf), -7),
+    (dict(o=P[0]), -11), (dict(lse=P[1]), -11), (dict(lse=P[3]), -11),
+    (dict(causal=2), -12), (dict(causal=-1), -12),
+])
+def test_forward_rejects_bad_arguments(L, kw, status):
+    assert fwd(**kw) == status
+
+
+def bwd(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], dO=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[8],
+             B=2, H=3, N=100, d=128, scale=0.088, causal=1, dtype=fa.FATTN_BF16, ws=P[9],
+             wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = fa.fattn_bwd_workspace_size(a["B"], a["H"], a["N"], a["d"], a["dtype"]) if a["dtype"] in (1, 2) and a["d"] in (64, 128) and min(a["B"], a["H"], a["N"]) > 0 else 0
+    return fa.fattn_bwd(a["q"], a["k"], a["v"], a["o"], a["dO"], a["lse"], a["dq"], a["dk"], a["dv"],
+                        a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], a["ws"],
+                        a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(dO=None), -1), (dict(lse=None), -1), (dict(dv=None), -1),
+    (dict(N=0), -2), (dict(H=0), -2),
+    (dict(d=80), -3),
+    (dict(dtype=fa.FATTN_F32), -4), (dict(dtype=9), -4),
+    (dict(dq=MIS), -6), (dict(k=MIS), -6),
+    (dict(scale=float("nan")), -7),
+    (dict(ws=None), -8), (dict(wsb=16), -8),
+    (dict(dq=P[0]), -11), (dict(dk=P[4]), -11), (dict(dv=P[6]), -11), (dict(ws=P[6]), -11), (dict(ws=P[1]), -11),
+    (dict(causal=3), -12),
+])
+def test_backward_rejects_bad_arguments(L, kw, status):
+    assert bwd(**kw) == status
+
+
+def test_workspace_size(L):
+    n = fa.fattn_bwd_workspace_size(2, 16, 4096, 128, fa.FATTN_BF16)
+    assert n >= 4 * 2 * 16 * 4096 and n % 256 == 0
+    assert fa.fattn_bwd_workspace_size(2, 16, 4096, 96, fa.FATTN_BF16) == 0
+    assert fa.fattn_bwd_workspace_size(0, 16, 4096, 128, fa.FATTN_BF16) == 0
+    assert fa.fattn_bwd_workspace_size(1, 1, 16, 64, fa.FATTN_F32) == 0
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)

@@ -1,0 +1,278 @@
+"""Forward parity of the HIP path (through the C ABI) against the float64 oracle.
+
+Inputs are the seeded generator's rounded tensors; the oracle runs on exactly the same values.
+Tolerances (float32: O max-abs 1e-5; fp16/bf16: O max-abs 1e-2 and per-slice max-rel 2e-2;
+LSE max-abs 1e-3) are the ones in oracle.metrics.TOL.
+"""
+import functools
+import math
+
+import numpy as np
+import pytest
+
+import fattn_inputs as fi
+from oracle import attention as att
+from oracle import metrics as M
+from tests.gpu_util import from_dev, log, sample_heads, to_dev, upload
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["f32", "f16", "bf16"]
+
+
+def _fa():
+    import io_aware_tiled_fattn_amd as fa
+    return fa
+
+
+def _check(o, lse, o_ref, lse_ref, dtype, lse_tol=None, o_abs_factor=1.0):
+    tol = M.TOL[dtype]
+    ea = M.max_abs(o, o_ref)
+    er = M.max_rel(o, o_ref)
+    el = M.max_abs(lse, lse_ref)
+    log(f"    O max-abs {ea:.3e} max-rel {er:.3e}  LSE max-abs {el:.3e}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert ea <= tol["o_abs"] * o_abs_factor, ea
+    if tol["o_rel"] is not None:
+        assert er <= tol["o_rel"], er
+    assert el <= (lse_tol if lse_tol is not None else tol["lse_abs"]), el
+
+
+def _run(inp, causal, scale=None, Br=0, Bc=0):
+    fa = _fa()
+    q, k, v, _ = upload(inp)
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale, Br=Br, Bc=Bc)
+    import torch
+    torch.cuda.synchronize()
+    return from_dev(o), from_dev(lse)
+
+
+# --------------------------------------------------------------------------------------------
+# Small shapes spanning several tiles, ragged tails and the degenerate N = 1, 2, 3.
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 2, 3, 65, 100, 129, 257, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_small_shapes(dtype, d, N, causal):
+    B, H = 1, 2
+    log(f"fwd small dtype={dtype} d={d} N={N} causal={causal}")
+    inp = fi.make_inputs((B, H, N, d), dtype, 100 + N)
+    scale = 1 / math.sqrt(d)
+    o, lse = _run(inp, causal)
+    o_ref, lse_ref = att.forward(inp.q, inp.k, inp.v, scale, causal)
+    _check(o, lse, o_ref, lse_ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("tile", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_every_tile_shape(dtype, tile, causal):
+    B, H, N, d = 2, 2, 333, 128
+    log(f"fwd tile {tile} dtype={dtype} causal={causal}")
+    inp = fi.make_inputs((B, H, N, d), dtype, 7)
+    o, lse = _run(inp, causal, Br=tile[0], Bc=tile[1])
+    o_ref, lse_ref = att.forward(inp.q, inp.k, inp.v, 1 / math.sqrt(d), causal)
+    _check(o, lse, o_ref, lse_ref, dtype)
+
+
+@pytest.mark.parametrize("tile", [(64, 32), (128, 32)])
+def test_forward_f32_tiles(tile):
+    inp = fi.make_inputs((1, 2, 200, 64), "f32", 8)
+    for causal in (False, True):
+        o, lse = _run(inp, causal, Br=tile[0], Bc=tile[1])
+        o_ref, lse_ref = att.forward(inp.q, inp.k, inp.v, 1 / 8, causal)
+        _check(o, lse, o_ref, lse_ref, "f32")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("scale", [0.0, -0.2, 1.3])
+def test_forward_unusual_scales(dtype, scale):
+    d = 64
+    inp = fi.make_inputs((1, 2, 150, d), dtype, 9)
+    # The float32 bound is stated at scale = 1/sqrt(d). Logits grow with |scale| sqrt(d), and the
+    # float32 rounding of a logit (relative 2^-24) moves its weight by that much relative, so the
+    # absolute error of O and LSE grows in proportion.
+    # For 16-bit outputs the absolute bound is stated for |O| well below 1; a sharp softmax makes
+    # O close to single value rows (|O| up to ~4), where rounding O and P to 8 significant bits
+    # alone costs about 2^-8 |O|, so the bound becomes max(1e-2, 2^-7 max|O|) (max-rel unchanged).
+    factor = max(1.0, abs(scale) * math.sqrt(d)) if dtype == "f32" else 1.0
+    for causal in (False, True):
+        o, lse = _run(inp, causal, scale=scale)
+        o_ref, lse_ref = att.forward(inp.q, inp.k, inp.v, scale, causal)
+        f_o = factor
+        if dtype != "f32":
+            f_o = max(1.0, 2.0 ** -7 * float(np.max(np.abs(o_ref))) / M.TOL[dtype]["o_abs"])
+        _check(o, lse, o_ref, lse_ref, dtype, lse_tol=M.TOL[dtype]["lse_abs"] * factor, o_abs_factor=f_o)
+
+
+# --------------------------------------------------------------------------------------------
+# The pages' worked example, embedded at d = 64 (zero padding leaves the logits unchanged).
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_forward_worked_example_fifty_thirds(dtype):
+    import torch
+    fa = _fa()
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    q = torch.zeros(1, 1, 2, 64)
+    k = torch.zeros(1, 1, 2, 64)
+    v = torch.zeros(1, 1, 2, 64)
+    q[..., 0] = 1.0
+    k[0, 0, 1, 0] = math.log(2.0)
+    v[0, 0, 0, 0], v[0, 0, 1, 0] = 10.0, 20.0
+    qd, kd, vd = (t.to(tdt).cuda() for t in (q, k, v))
+    o, lse = fa.forward(qd, kd, vd, scale=1.0)
+    o_nc = from_dev(o)
+    oc, lsec = fa.forward(qd, kd, vd, causal=True, scale=1.0)
+    o_c = from_dev(oc)
+    # oracle on the same rounded inputs (ln 2 is not exact in 16-bit types)
+    qr, kr, vr = (from_dev(t) for t in (qd, kd, vd))
+    o_ref, lse_ref = att.forward(qr, kr, vr, 1.0)
+    oc_ref, lsec_ref = att.forward(qr, kr, vr, 1.0, causal=True)
+    # |O| reaches 50/3 here, where one bf16 ulp is 0.125: the 16-bit absolute bound scales with
+    # max|O| as in test_forward_unusual_scales (max-rel stays at its stated value).
+    f_o = 1.0 if dtype == "f32" else max(1.0, 2.0 ** -7 * 20.0 / M.TOL[dtype]["o_abs"])
+    _check(o_nc, from_dev(lse), o_ref, lse_ref, dtype, o_abs_factor=f_o)
+    _check(o_c, from_dev(lsec), oc_ref, lsec_ref, dtype, o_abs_factor=f_o)
+    if dtype == "f32":
+        assert o_nc[0, 0, 0, 0] == pytest.approx(50 / 3, abs=1e-5)
+        assert o_nc[0, 0, 1, 0] == pytest.approx(50 / 3, abs=1e-5)
+        assert o_c[0, 0, 0, 0] == pytest.approx(10.0, abs=1e-5)
+        assert o_c[0, 0, 1, 0] == pytest.approx(50 / 3, abs=1e-5)
+        assert from_dev(lse)[0, 0, 0] == pytest.approx(math.log(3.0), abs=1e-6)
+    assert abs(o_nc[0, 0, 0, 0] - 30.0) > 10  # not the per-block-normalised sum
+
+
+# --------------------------------------------------------------------------------------------
+# The five workloads.
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_workload1_f32(causal):
+    w = fi.WORKLOADS[1]
+    inp = fi.workload_inputs(1)
+    o, lse = _run(inp, causal)
+    o_ref, lse_ref = att.forward(inp.q, inp.k, inp.v, w.scale, causal)
+    _check(o, lse, o_ref, lse_ref, "f32")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("variant", [0, 1, 2])
+def test_workload2_f16_with_shift(causal, variant):
+    w = fi.WORKLOADS[2]
+    log(f"workload 2 variant {variant} causal={causal}")
+    inp = fi.workload_inputs(2, variant)
+    o, lse = _run(inp, causal)
+    o_ref, lse_ref = att.forward(inp.q, inp.k, inp.v, w.scale, causal)
+    # Logits of the literal shift reach |s| ~ 2000, where one float32 ulp of s is 1.2e-4 and
+    # the 64-term dot product carries a few of them; the LSE bound scales with max |s|.
+    lse_tol = None
+    if variant == 2:
+        smax = float(np.max(np.abs(lse_ref)))
+        lse_tol = 1e-3 + 64 * smax * 2.0 ** -24
+    _check(o, lse, o_ref, lse_ref, "f16", lse_tol)
+    if variant == 1:
+        partner = fi.unshifted_partner(inp, w.scale)
+        o0, lse0 = _run(partner, causal)
+        assert M.max_abs(o, o0) <= 1e-2
+        assert M.max_abs(lse - lse0, 500.0) <= 2e-3
+        assert np.all(lse > 400)
+
+
+@functools.lru_cache(maxsize=1)
+def _workload(ident):
+    return fi.workload_inputs(ident, with_do=False)
+
+
+def _workload_heads(ident, causal, Br=0, Bc=0):
+    w = fi.WORKLOADS[ident]
+    inp = _workload(ident)
+    o, lse = _run(inp, causal, Br=Br, Bc=Bc)
+    heads = sample_heads(w.B, w.H, 2 if w.N > 8192 else 3)
+    o_ref, lse_ref = att.forward(inp.q, inp.k, inp.v, w.scale, causal, heads=heads)
+    for b, h in heads:
+        log(f"  head ({b},{h})")
+        _check(o[b, h], lse[b, h], o_ref[b, h], lse_ref[b, h], w.dtype)
+    return inp, o, lse
+
+
+@pytest.mark.parametrize("tile", [(0, 0), (64, 64), (64, 128), (128, 64), (128, 128)])
+def test_workload3_bf16_causal_tiles(tile):
+    log(f"workload 3 tile {tile}")
+    _workload_heads(3, True, *tile)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_workload4_bf16_long(causal):
+    log(f"workload 4 causal={causal}")
+    _workload_heads(4, causal)
+
+
+def test_workload5_forward():
+    _workload_heads(5, True)
+
+
+# --------------------------------------------------------------------------------------------
+# Invariants that hold at any size.
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_causal_prefix_is_bitwise_unchanged(dtype):
+    fa = _fa()
+    B, H, N, d = 1, 2, 700, 128 if dtype == "bf16" else 64
+    inp = fi.make_inputs((B, H, N, d), dtype, 11)
+    other = fi.make_inputs((B, H, N, d), dtype, 12)
+    q, k, v, _ = upload(inp)
+    o1, l1 = fa.forward(q, k, v, causal=True)
+    cut = 300
+    k2, v2 = k.clone(), v.clone()
+    _, ko, vo, _ = upload(other)
+    k2[:, :, cut + 1:] = ko[:, :, cut + 1:]
+    v2[:, :, cut + 1:] = vo[:, :, cut + 1:]
+    o2, l2 = fa.forward(q, k2, v2, causal=True)
+    import torch
+    assert torch.equal(o1[:, :, : cut + 1], o2[:, :, : cut + 1])
+    assert torch.equal(l1[:, :, : cut + 1], l2[:, :, : cut + 1])
+    assert not torch.equal(o1[:, :, cut + 1:], o2[:, :, cut + 1:])
+
+
+def test_k_zero_gives_prefix_means_at_full_shape():
+    import torch
+    fa = _fa()
+    w = fi.WORKLOADS[3]
+    inp = fi.make_inputs(w.shape, "bf16", 13)
+    _, _, v, _ = upload(inp)
+    q = v.clone()
+    k = torch.zeros_like(v)
+    o, lse = fa.forward(q, k, v, causal=True)
+    vf = v.float()
+    ref = torch.cumsum(vf, dim=2) / torch.arange(1, w.N + 1, device=v.device, dtype=torch.float32)[:, None]
+    assert float((o.float() - ref).abs().max()) <= 1e-2
+    lref = torch.log(torch.arange(1, w.N + 1, device=v.device, dtype=torch.float32))
+    assert float((lse - lref).abs().max()) <= 1e-3
+
+
+def test_run_to_run_deterministic():
+    import torch
+    fa = _fa()
+    inp = fi.make_inputs((2, 4, 1024, 128), "bf16", 14)
+    q, k, v, _ = upload(inp)
+    o1, l1 = fa.forward(q, k, v, causal=True)
+    o2, l2 = fa.forward(q, k, v, causal=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_forward_on_a_side_stream():
+    import torch
+    fa = _fa()
+    inp = fi.make_inputs((1, 4, 512, 64), "f16", 15)
+    q, k, v, _ = upload(inp)
+    ref_o, ref_l = fa.forward(q, k, v, causal=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o, l = fa.forward(q, k, v, causal=True, stream=s)
+    s.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
