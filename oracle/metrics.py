@@ -29,8 +29,12 @@ def max_abs(x, r):
     return float(np.max(np.abs(x - r)))
 
 
-def max_rel(x, r, slice_ndim: int = 2):
-    """Per-slice relative error; slices are the trailing ``slice_ndim`` axes."""
+def max_rel(x, r, slice_ndim: int = 2, floor: float = 0.0):
+    """Per-slice relative error; slices are the trailing ``slice_ndim`` axes.
+
+    ``floor`` bounds the denominator from below: where the exact result of a slice is identically
+    zero (dQ and dK of a one-key sequence), the error is measured against ``floor`` instead.
+    """
     x = np.asarray(x, np.float64)
     r = np.asarray(r, np.float64)
     if x.size == 0:
@@ -40,7 +44,7 @@ def max_rel(x, r, slice_ndim: int = 2):
     rs = r.reshape((-1,) + r.shape[r.ndim - slice_ndim:])
     worst = 0.0
     for a, b in zip(xs, rs):
-        den = float(np.max(np.abs(b)))
+        den = max(float(np.max(np.abs(b))), floor)
         num = float(np.max(np.abs(a - b)))
         if den == 0.0:
             rel = 0.0 if num == 0.0 else np.inf
