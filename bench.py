@@ -1,18 +1,20 @@
 """Benchmark: attention forward/backward TFLOP/s on one MI355X at N=4096, d=128 (bf16, causal).
 
-A step is one pass of the whole hot path over one batch: fattn_fwd then fattn_bwd on the
-training-shaped workload B=2, H=16, N=4096, d=128 (causal, bf16; Q, K, V, dO iid N(0,1) from a
-seed). FLOPs per step follow the stated convention: forward 4*B*H*N^2*d halved for causal,
-backward 2.5x the forward. The forward alone is also timed on the prefill workload B=4, H=16.
+A step is one pass of the whole hot path over one batch: fattn_fwd then fattn_bwd (rowsum(dO*O),
+dK/dV, dQ) on the training-shaped workload B=2, H=16, N=4096, d=128 (causal, bf16; Q, K, V, dO
+iid N(0,1) from a seed). FLOPs per step follow the stated convention: forward 4*B*H*N^2*d halved
+for causal, backward 2.5x the forward. The forward alone is also timed on the prefill workload
+B=4, H=16, N=4096.
 
-Timing: HIP events on the stream the kernels run on (torch's current stream), after warm-up,
-inputs resident in HBM. Prints ONE JSON line.
+Timing: HIP events on the stream the kernels are launched on (torch's current stream), after
+warm-up, inputs resident in HBM. Every kernel of the step is also timed on its own (one launch
+per call), which gives the dominant kernel's per-launch time for the roofline object. Prints ONE
+JSON line.
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -21,7 +23,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
+# MI355X published dense peaks: bf16 MFMA 2.5 PFLOP/s (256 CU x 2.4 GHz x 4096 FLOP/clk/CU),
+# HBM3E 8 TB/s.
+PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 
 
@@ -56,7 +60,6 @@ def _time_calls(fn, steps, warmup, torch):
 
 def cpu_oracle_baseline(budget_s: float = 20.0):
     """Time the float64 oracle on a bounded sample of the step's workload (host cores)."""
-    import numpy as np
     import fattn_inputs as fi
     from oracle import attention as att
     try:
@@ -88,71 +91,96 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--fwd-only", action="store_true", help="time only the forward")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB read + 256 MiB write elementwise copy, so HBM "
+                         "byte counters can be scaled by a kernel of known traffic")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the kernels shard over (batch, head) with no "
-              "communication, so N>1 runs are not provided", file=sys.stderr)
+              "communication, so runs on more than one GPU are not provided", file=sys.stderr)
         return 2
 
     import torch
     import fattn_inputs as fi
     import io_aware_tiled_fattn_amd as fa
+    from io_aware_tiled_fattn_amd import profiling
 
     fa.lib()
     w5, w3 = fi.WORKLOADS[5], fi.WORKLOADS[3]
+    B, H, N, d = w5.shape
 
     # Training-shaped step: forward + backward.
     inp5 = fi.workload_inputs(5)
     q, k, v, do = _upload(inp5, torch)
-    o, lse = fa.forward(q, k, v, causal=True)
-    have_bwd = not a.fwd_only
-    if have_bwd:
-        try:
-            ws = torch.empty(fa.fattn_bwd_workspace_size(w5.B, w5.H, w5.N, w5.d, fa.FATTN_BF16),
-                             dtype=torch.uint8, device="cuda")
-            fa.backward(q, k, v, o, do, lse, causal=True, workspace=ws)
-        except fa.FattnError:
-            have_bwd = False
-
-    fwd5 = lambda: fa.forward(q, k, v, causal=True, out=o, lse=lse)
-    ms_fwd5 = _time_calls(fwd5, a.steps, a.warmup, torch)
-    f_fwd5 = flops_fwd(w5.B, w5.H, w5.N, w5.d, True)
-    result = {}
-    if have_bwd:
-        bwd5 = lambda: fa.backward(q, k, v, o, do, lse, causal=True, workspace=ws)
-        ms_bwd5 = _time_calls(bwd5, a.steps, a.warmup, torch)
-
-        def step():
-            fa.forward(q, k, v, causal=True, out=o, lse=lse)
-            fa.backward(q, k, v, o, do, lse, causal=True, workspace=ws)
-
-        ms_step = _time_calls(step, a.steps, a.warmup, torch)
-        f_step = 3.5 * f_fwd5
-        workload = "training step fwd+bwd: B=2,H=16,N=4096,d=128 causal bf16"
-    else:
-        ms_bwd5 = None
-        ms_step = ms_fwd5
-        f_step = f_fwd5
-        workload = "forward only (backward not built): B=2,H=16,N=4096,d=128 causal bf16"
     del inp5
+    o, lse = fa.forward(q, k, v, causal=True)
+    ws = torch.empty(fa.fattn_bwd_workspace_size(B, H, N, d, fa.FATTN_BF16), dtype=torch.uint8, device="cuda")
+    dvec = ws[: 4 * B * H * N].view(torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa.backward(q, k, v, o, do, lse, causal=True, workspace=ws)
+
+    T = lambda fn: _time_calls(fn, a.steps, a.warmup, torch)
+    st = lambda stages: (lambda: fa.backward_stages(q, k, v, o, do, lse, dq, dk, dv, dvec, causal=True,
+                                                    stages=stages))
+    ms = {
+        "fwd": T(lambda: fa.forward(q, k, v, causal=True, out=o, lse=lse)),
+        "pre": T(st((0,))),
+        "dkdv": T(st((1,))),
+        "dq": T(st((2,))),
+        "bwd": T(lambda: fa.backward(q, k, v, o, do, lse, causal=True, workspace=ws)),
+    }
+
+    def step():
+        fa.forward(q, k, v, causal=True, out=o, lse=lse)
+        fa.backward(q, k, v, o, do, lse, causal=True, workspace=ws)
+
+    ms_step = T(step)
 
     # Prefill-shaped forward (B=4).
     inp3 = fi.workload_inputs(3)
     q3, k3, v3, _ = _upload(inp3, torch)
-    o3, l3 = fa.forward(q3, k3, v3, causal=True)
-    ms_fwd3 = _time_calls(lambda: fa.forward(q3, k3, v3, causal=True, out=o3, lse=l3), a.steps, a.warmup, torch)
-    f_fwd3 = flops_fwd(w3.B, w3.H, w3.N, w3.d, True)
     del inp3
+    o3, l3 = fa.forward(q3, k3, v3, causal=True)
+    ms_fwd3 = T(lambda: fa.forward(q3, k3, v3, causal=True, out=o3, lse=l3))
+    del q3, k3, v3, o3, l3
 
-    tf = lambda f, ms: f / (ms * 1e-3) / 1e12
+    if a.calibrate_copy:
+        src = torch.ones(128 * 2**20, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    tf = lambda f, t: f / (t * 1e-3) / 1e12
+    f_fwd = flops_fwd(B, H, N, d, True)
+    f_step = 3.5 * f_fwd
     value = tf(f_step, ms_step)
-    fwd3_tf = tf(f_fwd3, ms_fwd3)
-    # Dominant kernel = the forward kernel while it is the only one; its per-launch time is the
-    # event-timed fattn_fwd call (one kernel per call).
-    roof = {"kernel": "fwd_kernel<bf16,d128,Br128,Bc64,causal> on B=4,H=16,N=4096",
-            "bound": "mfma", "achieved": round(fwd3_tf, 1), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(fwd3_tf / PEAK_BF16_TFLOPS, 4), "traffic": None}
+
+    # Algorithmic FLOPs per launch of each matmul kernel (causal halves every GEMM):
+    # forward 2 GEMMs, dK/dV 4 (S, dP, dV, dK), dQ 3 (S, dP, dQ), each 2*N^2*d per head.
+    kernels = {
+        "fwd": ("fwd_kernel", f_fwd, 1024 * 256),
+        "dkdv": ("bwd_dkdv_kernel", 2 * f_fwd, 1024 * 256),
+        "dq": ("bwd_dq_kernel", 1.5 * f_fwd, 1024 * 256),
+    }
+    dom = max(kernels, key=lambda k_: ms[k_])
+    name, fl, grid = kernels[dom]
+    achieved = tf(fl, ms[dom])
+    traffic = None
+    tr = profiling.load_traffic(os.path.join(ROOT, "profiles"))
+    if tr:
+        for (kname, kgrid), rec in tr.items():
+            if kname.startswith(name) and "Bf16, 128, true" in kname and kgrid == grid:
+                traffic = {"fetch_bytes": round(rec["fetch_bytes"]), "write_bytes": round(rec["write_bytes"]),
+                           "source": "profiles/traffic.json"}
+    roof = {"kernel": f"{name}<bf16, d=128, causal> on B=2,H=16,N=4096", "bound": "mfma",
+            "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+            "ms_per_launch": round(ms[dom], 4), "algorithmic_tflop_per_launch": round(fl / 1e12, 4)}
+
+    fwd3_tf = tf(flops_fwd(w3.B, w3.H, w3.N, w3.d, True), ms_fwd3)
+    bwd_tf = tf(2.5 * f_fwd, ms["bwd"])
     result = {
         "metric": "attention fwd/bwd TFLOP/s and % of MI355X bf16 MFMA peak at N=4096, d=128",
         "value": round(value, 1),
@@ -166,17 +194,16 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": workload, "B": w5.B, "H": w5.H, "N": w5.N, "d": w5.d, "causal": True},
+        "config": {"workload": "training step fwd+bwd, B=2 H=16 N=4096 d=128 causal",
+                   "B": B, "H": H, "N": N, "d": d, "causal": True},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "fwd": {"workload": "B=4,H=16,N=4096,d=128 causal bf16", "ms": round(ms_fwd3, 4),
+        "fwd": {"workload": "B=4 H=16 N=4096 d=128 causal", "ms": round(ms_fwd3, 4),
                 "tflops": round(fwd3_tf, 1), "frac_of_peak": round(fwd3_tf / PEAK_BF16_TFLOPS, 4)},
-        "fwd_b2": {"ms": round(ms_fwd5, 4), "tflops": round(tf(f_fwd5, ms_fwd5), 1)},
+        "bwd": {"workload": "B=2 H=16 N=4096 d=128 causal", "ms": round(ms["bwd"], 4),
+                "tflops": round(bwd_tf, 1), "frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "kernel_ms": {k_: round(t, 4) for k_, t in ms.items()},
         "roofline": roof,
     }
-    if ms_bwd5 is not None:
-        bt = tf(2.5 * f_fwd5, ms_bwd5)
-        result["bwd"] = {"workload": "B=2,H=16,N=4096,d=128 causal bf16", "ms": round(ms_bwd5, 4),
-                         "tflops": round(bt, 1), "frac_of_peak": round(bt / PEAK_BF16_TFLOPS, 4)}
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_oracle_baseline()
     print(json.dumps(result), flush=True)

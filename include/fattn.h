@@ -82,9 +82,9 @@ int fattn_fwd_tiled(const void* q, const void* k, const void* v, void* o, float*
                     int Br, int Bc, void* stream);
 
 /*
- * Bytes of device workspace fattn_bwd needs: the float32 row vector D = rowsum(dO * O)
- * [B,H,N] plus the float32 dQ accumulator [B,H,N,d]. Returns 0 for arguments that fattn_bwd would
- * reject on shape, head dim or dtype grounds.
+ * Bytes of device workspace fattn_bwd needs: the float32 row vector D = rowsum(dO * O) [B,H,N],
+ * rounded up to 256 bytes. Returns 0 for arguments that fattn_bwd would reject on shape, head
+ * dim or dtype grounds.
  */
 size_t fattn_bwd_workspace_size(int B, int H, int N, int d, int dtype);
 
@@ -100,6 +100,24 @@ int fattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
               const float* lse, void* dq, void* dk, void* dv,
               int B, int H, int N, int d, float scale, int causal, int dtype,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The three stages of fattn_bwd, in the order fattn_bwd enqueues them, for callers that want to
+ * schedule or time them separately. Same conventions and checks as fattn_bwd; `dvec` is the
+ * float32 [B,H,N] row vector D = rowsum(dO * O) (the first bytes of fattn_bwd's workspace).
+ *   fattn_bwd_preprocess: reads o, dO; writes dvec.
+ *   fattn_bwd_dkdv:       reads q, k, v, dO, lse, dvec; writes dk, dv (per key tile, recomputing
+ *                         P = exp(S - LSE) for every query tile on or below the diagonal).
+ *   fattn_bwd_dq:         reads q, k, v, dO, lse, dvec; writes dq (per query tile).
+ */
+int fattn_bwd_preprocess(const void* o, const void* dO, float* dvec, int B, int H, int N, int d,
+                         int dtype, void* stream);
+int fattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                   const float* dvec, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                   int causal, int dtype, void* stream);
+int fattn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                 const float* dvec, void* dq, int B, int H, int N, int d, float scale, int causal,
+                 int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fattn_strerror(int status);

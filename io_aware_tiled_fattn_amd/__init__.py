@@ -5,8 +5,9 @@ C ABI declared in include/fattn.h. PyTorch is used to allocate device memory and
 stream; there is no CPU or PyTorch fallback, and a missing library raises.
 
 Low-level names mirror the C entry points (``fattn_fwd``, ``fattn_fwd_tiled``, ``fattn_bwd``,
-``fattn_bwd_workspace_size``, ``fattn_strerror``, ``fattn_version``) and take raw device
-addresses. ``forward`` and ``backward`` wrap them for contiguous [B, H, N, d] torch tensors.
+``fattn_bwd_workspace_size``, ``fattn_bwd_preprocess``, ``fattn_bwd_dkdv``, ``fattn_bwd_dq``,
+``fattn_strerror``, ``fattn_version``) and take raw device addresses. ``forward``, ``backward``
+and ``backward_stages`` wrap them for contiguous [B, H, N, d] torch tensors.
 """
 from __future__ import annotations
 
@@ -17,7 +18,8 @@ import os
 __all__ = [
     "FATTN_F32", "FATTN_F16", "FATTN_BF16", "FattnError", "lib", "library_path",
     "fattn_fwd", "fattn_fwd_tiled", "fattn_bwd", "fattn_bwd_workspace_size", "fattn_strerror",
-    "fattn_version", "forward", "backward", "dtype_code",
+    "fattn_bwd_preprocess", "fattn_bwd_dkdv", "fattn_bwd_dq",
+    "fattn_version", "forward", "backward", "backward_stages", "dtype_code",
 ]
 
 FATTN_F32, FATTN_F16, FATTN_BF16 = 0, 1, 2
@@ -55,6 +57,12 @@ def lib():
     L.fattn_bwd_workspace_size.restype = sz
     L.fattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
     L.fattn_bwd.restype = i
+    L.fattn_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
+    L.fattn_bwd_preprocess.restype = i
+    L.fattn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    L.fattn_bwd_dkdv.restype = i
+    L.fattn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    L.fattn_bwd_dq.restype = i
     L.fattn_strerror.argtypes = [i]
     L.fattn_strerror.restype = ctypes.c_char_p
     L.fattn_version.argtypes = []
@@ -82,6 +90,18 @@ def fattn_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype,
               workspace, workspace_bytes, stream=None) -> int:
     return lib().fattn_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype,
                            workspace, workspace_bytes, stream)
+
+
+def fattn_bwd_preprocess(o, dO, dvec, B, H, N, d, dtype, stream=None) -> int:
+    return lib().fattn_bwd_preprocess(o, dO, dvec, B, H, N, d, dtype, stream)
+
+
+def fattn_bwd_dkdv(q, k, v, dO, lse, dvec, dk, dv, B, H, N, d, scale, causal, dtype, stream=None) -> int:
+    return lib().fattn_bwd_dkdv(q, k, v, dO, lse, dvec, dk, dv, B, H, N, d, scale, causal, dtype, stream)
+
+
+def fattn_bwd_dq(q, k, v, dO, lse, dvec, dq, B, H, N, d, scale, causal, dtype, stream=None) -> int:
+    return lib().fattn_bwd_dq(q, k, v, dO, lse, dvec, dq, B, H, N, d, scale, causal, dtype, stream)
 
 
 def fattn_strerror(status: int) -> str:
@@ -163,3 +183,27 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, stre
     if st != 0:
         raise FattnError(st, "fattn_bwd")
     return dq, dk, dv
+
+
+def backward_stages(q, k, v, o, do, lse, dq, dk, dv, dvec, causal=False, scale=None, stream=None,
+                    stages=(0, 1, 2)):
+    """Run the chosen stages of the backward (0: D = rowsum(dO*O), 1: dK/dV, 2: dQ) into
+    preallocated outputs; ``dvec`` is a float32 [B, H, N] device tensor."""
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = dtype_code(q)
+    s = _stream(stream)
+    for stage in stages:
+        if stage == 0:
+            st = fattn_bwd_preprocess(o.data_ptr(), do.data_ptr(), dvec.data_ptr(), B, H, N, d, code, s)
+        elif stage == 1:
+            st = fattn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                                dvec.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale),
+                                int(bool(causal)), code, s)
+        else:
+            st = fattn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                              dvec.data_ptr(), dq.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                              code, s)
+        if st != 0:
+            raise FattnError(st, f"backward stage {stage}")

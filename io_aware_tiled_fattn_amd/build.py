@@ -24,6 +24,9 @@ COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs: the softmax reads them every tile, and AGPR<->VGPR copies
+    # cost both instructions and registers
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result", "-Wno-unused-command-line-argument",
     f"-I{os.path.join(ROOT, 'include')}",
 ]

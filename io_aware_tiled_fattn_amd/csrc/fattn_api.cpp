@@ -120,4 +120,57 @@ int fattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
   return launch_status(fattn::launch_bwd(r, (hipStream_t)stream));
 }
 
+int fattn_bwd_preprocess(const void* o, const void* dO, float* dvec, int B, int H, int N, int d,
+                         int dtype, void* stream) {
+  if (!o || !dO || !dvec) return FATTN_ERR_NULL;
+  int st = check_common(B, H, N, d, dtype);
+  if (st != FATTN_OK) return st;
+  if (dtype == FATTN_F32) return FATTN_ERR_DTYPE;
+  if (!aligned16(o) || !aligned16(dO) || !aligned16(dvec)) return FATTN_ERR_ALIGN;
+  if ((const void*)dvec == o || (const void*)dvec == dO) return FATTN_ERR_ALIAS;
+  fattn::BwdReq r{nullptr, nullptr, nullptr, o, dO, nullptr, nullptr, nullptr, nullptr,
+                  B, H, N, d, 1.0f, 0, dtype, dvec};
+  return launch_status(fattn::launch_bwd(r, (hipStream_t)stream, 0));
+}
+
+static int check_stage(const void* q, const void* k, const void* v, const void* dO,
+                       const float* lse, const float* dvec, void* out0, void* out1,
+                       int B, int H, int N, int d, float scale, int causal, int dtype) {
+  if (!q || !k || !v || !dO || !lse || !dvec || !out0) return FATTN_ERR_NULL;
+  int st = check_common(B, H, N, d, dtype);
+  if (st != FATTN_OK) return st;
+  if (dtype == FATTN_F32) return FATTN_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FATTN_ERR_CAUSAL;
+  if (!std::isfinite(scale)) return FATTN_ERR_SCALE;
+  const void* ins[6] = {q, k, v, dO, lse, dvec};
+  for (const void* p : ins)
+    if (!aligned16(p)) return FATTN_ERR_ALIGN;
+  if (!aligned16(out0) || (out1 && !aligned16(out1))) return FATTN_ERR_ALIGN;
+  for (const void* p : ins)
+    if (p == out0 || (out1 && p == out1)) return FATTN_ERR_ALIAS;
+  if (out1 && out0 == out1) return FATTN_ERR_ALIAS;
+  return FATTN_OK;
+}
+
+int fattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                   const float* dvec, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                   int causal, int dtype, void* stream) {
+  if (!dv) return FATTN_ERR_NULL;
+  int st = check_stage(q, k, v, dO, lse, dvec, dk, dv, B, H, N, d, scale, causal, dtype);
+  if (st != FATTN_OK) return st;
+  fattn::BwdReq r{q, k, v, nullptr, dO, lse, nullptr, dk, dv, B, H, N, d, scale, causal, dtype,
+                  (float*)dvec};
+  return launch_status(fattn::launch_bwd(r, (hipStream_t)stream, 1));
+}
+
+int fattn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                 const float* dvec, void* dq, int B, int H, int N, int d, float scale, int causal,
+                 int dtype, void* stream) {
+  int st = check_stage(q, k, v, dO, lse, dvec, dq, nullptr, B, H, N, d, scale, causal, dtype);
+  if (st != FATTN_OK) return st;
+  fattn::BwdReq r{q, k, v, nullptr, dO, lse, dq, nullptr, nullptr, B, H, N, d, scale, causal, dtype,
+                  (float*)dvec};
+  return launch_status(fattn::launch_bwd(r, (hipStream_t)stream, 2));
+}
+
 }  // extern "C"

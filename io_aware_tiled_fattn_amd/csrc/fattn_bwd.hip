@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int h = lane >> 5;
   const int lr = lane & 31;
   const int N = a.N;
@@ -218,13 +218,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           dp[e] = 0.f;
         }
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
+        for (int st = 0; st < D / 16; ++st) {  // two independent chains, interleaved
           const vec8 qa = *(const vec8*)(Qs + (qb * 32 + lr) * Cfg::STR + 16 * st + 8 * h);
-          s = TR::mma(qa, kf[st], s);
-        }
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
           const vec8 da = *(const vec8*)(dOs + (qb * 32 + lr) * Cfg::STR + 16 * st + 8 * h);
+          s = TR::mma(qa, kf[st], s);
           dp = TR::mma(da, vf[st], dp);
         }
         // element 4j + r is query qb*32 + 8j + 4h + r of the tile, key = this lane's key
@@ -236,8 +233,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int e = 4 * j + r;
-            float pv = __builtin_amdgcn_exp2f(s[e] * a.c - l4[r]);
-            if (need_mask && key > q_base + qb * 32 + 8 * j + 4 * h + r) pv = 0.f;
+            float pv = __builtin_amdgcn_exp2f(fmaf(s[e], a.c, -l4[r]));
+            if (need_mask) pv = (key > q_base + qb * 32 + 8 * j + 4 * h + r) ? 0.f : pv;
             p[e] = pv;
             ds[e] = pv * (dp[e] - d4[r]);
           }
@@ -318,7 +315,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int h = lane >> 5;
   const int lr = lane & 31;
   const int N = a.N;
@@ -414,13 +411,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
           dp[e] = 0.f;
         }
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
+        for (int st = 0; st < D / 16; ++st) {  // two independent chains, interleaved
           const vec8 ka = *(const vec8*)(Ks + (kb * 32 + lr) * Cfg::KSTR + 16 * st + 8 * h);
-          s = TR::mma(ka, qf[st], s);
-        }
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
           const vec8 va = *(const vec8*)(Vs + (kb * 32 + lr) * Cfg::VSTR + 16 * st + 8 * h);
+          s = TR::mma(ka, qf[st], s);
           dp = TR::mma(va, df[st], dp);
         }
         // element e is key k0 + kb*32 + 8(e>>2) + 4h + (e&3), query qrow
@@ -433,10 +427,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
               const int e = 8 * half + 2 * e2 + u;
-              float pv = __builtin_amdgcn_exp2f(s[e] * a.c - lse2);
+              float pv = __builtin_amdgcn_exp2f(fmaf(s[e], a.c, -lse2));
               if (need_mask) {
                 const int kk = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-                if (kk >= N || (CAUSAL && kk > qrow)) pv = 0.f;
+                pv = (kk >= N || (CAUSAL && kk > qrow)) ? 0.f : pv;
               }
               ds2[u] = pv * (dp[e] - dval);
             }
@@ -477,7 +471,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------------------------
 
 template <typename TR, int D>
-hipError_t launch_all(const BwdReq& r, hipStream_t st) {
+hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
   BwdArgs a;
   a.q = (const uint16_t*)r.q;
   a.k = (const uint16_t*)r.k;
@@ -495,28 +489,34 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st) {
   const long long BH = (long long)r.B * r.H;
   const long long rows = BH * r.N;
 
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<TR, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
-                     a.o, a.dO, r.dvec, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  a.ntiles = (r.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
-  dim3 g1((unsigned)(BH * a.ntiles));
-  if (r.causal)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<TR, D, true>), g1, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<TR, D, false>), g1, dim3(256), 0, st, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  a.ntiles = (r.N + DqCfg<D>::BQ - 1) / DqCfg<D>::BQ;
-  dim3 g2((unsigned)(BH * a.ntiles));
-  if (r.causal)
-    hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true>), g2, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false>), g2, dim3(256), 0, st, a);
-  return hipGetLastError();
+  hipError_t e = hipSuccess;
+  if (stage < 0 || stage == 0) {
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL((bwd_pre_kernel<TR, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
+                       a.o, a.dO, r.dvec, rows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stage < 0 || stage == 1) {
+    a.ntiles = (r.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
+    dim3 g1((unsigned)(BH * a.ntiles));
+    if (r.causal)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<TR, D, true>), g1, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<TR, D, false>), g1, dim3(256), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stage < 0 || stage == 2) {
+    a.ntiles = (r.N + DqCfg<D>::BQ - 1) / DqCfg<D>::BQ;
+    dim3 g2((unsigned)(BH * a.ntiles));
+    if (r.causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true>), g2, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false>), g2, dim3(256), 0, st, a);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace
@@ -527,9 +527,11 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   return (dvec + 255) & ~(size_t)255;
 }
 
-hipError_t launch_bwd(const BwdReq& r, hipStream_t st) {
-  if (r.dtype == FATTN_BF16) return r.d == 64 ? launch_all<Bf16, 64>(r, st) : launch_all<Bf16, 128>(r, st);
-  if (r.dtype == FATTN_F16) return r.d == 64 ? launch_all<F16, 64>(r, st) : launch_all<F16, 128>(r, st);
+hipError_t launch_bwd(const BwdReq& r, hipStream_t st, int stage) {
+  if (r.dtype == FATTN_BF16)
+    return r.d == 64 ? launch_all<Bf16, 64>(r, st, stage) : launch_all<Bf16, 128>(r, st, stage);
+  if (r.dtype == FATTN_F16)
+    return r.d == 64 ? launch_all<F16, 64>(r, st, stage) : launch_all<F16, 128>(r, st, stage);
   return hipErrorInvalidValue;
 }
 

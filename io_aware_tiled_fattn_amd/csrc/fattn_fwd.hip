@@ -43,8 +43,9 @@ struct FwdArgs {
   float* lse;
   int N;
   int n_qtiles;
-  float c;            // |scale| * log2(e)
-  uint32_t neg_mask;  // 0x80008000 flips the sign of two packed 16-bit Q elements (scale < 0)
+  float c;             // |scale| * log2(e), > 0
+  uint32_t neg_mask;   // 0x80008000 flips the sign of two packed 16-bit Q elements (scale < 0)
+  uint32_t keep_mask;  // 0 zeroes Q (scale == 0: every logit is 0), else all ones
 };
 
 template <int D, int BR, int BC>
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int h = lane >> 5;
   const int lr = lane & 31;
   const int N = a.N;
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   for (int s = 0; s < D / 16; ++s) {
     u32x4 raw = {0u, 0u, 0u, 0u};
     if (qrow < N) raw = *(const u32x4*)(Qh + (size_t)qrow * D + 16 * s + 8 * h);
-    raw ^= a.neg_mask;
+    raw = (raw ^ a.neg_mask) & a.keep_mask;
     qf[s] = bitcast<vec8>(raw);
   }
 
@@ -154,34 +155,40 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
       const uint16_t* Vs = Ks + Cfg::KBUF;
 
       // S^T = K Q^T for BC/32 blocks of 32 keys.
+      // (the BC/32 accumulators are independent chains, interleaved step by step)
       f32x16 s[BC / 32];
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
+      for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
+      for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb) {
           const vec8 kf = *(const vec8*)(Ks + (kb * 32 + lr) * Cfg::KSTR + 16 * st + 8 * h);
           s[kb] = TR::mma(kf, qf[st], s[kb]);
         }
-      }
 
-      // Scale into the log2 domain, mask, row max.
+      // Mask (diagonal and ragged tiles only), then the row max of the raw scores.
       const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
+      if (need_mask) {
+        // element (kb, e) holds key k0 + kb*32 + 8(e>>2) + 4h + (e&3); it is masked when that
+        // relative index exceeds lim
+        int lim = N - 1 - k0;
+        if (CAUSAL) lim = min(lim, qrow - k0);
+        lim -= 4 * h;
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            s[kb][e] = (kb * 32 + 8 * (e >> 2) + (e & 3) > lim) ? -__builtin_inff() : s[kb][e];
+      }
       float mx = -__builtin_inff();
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float t = s[kb][e] * a.c;
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (key >= N || (CAUSAL && key > qrow)) t = -__builtin_inff();
-          }
-          s[kb][e] = t;
-          mx = fmaxf(mx, t);
-        }
-      mx = max_halves(mx);
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+      mx = max_halves(mx) * a.c;  // c > 0, so this is the max of the log2-domain logits
 
       // Move the reference max only when it grew by more than the slack.
       const float m_new = fmaxf(m_ref, mx);
@@ -196,7 +203,9 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
           for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
       }
 
-      // P^T = exp2(t - m_ref), packed to 16-bit MFMA B fragments (8 keys per 16-key chunk).
+      // P^T = exp2(s*c - m_ref) (masked scores are -inf and give 0), packed to 16-bit MFMA B
+      // fragments (8 keys per 16-key chunk).
+      const float neg_m = -m_ref;
       vec8 pf[BC / 16];
       float ls = 0.f;
 #pragma unroll
@@ -206,8 +215,8 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
           u32x4 packed;
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
-            const float p0 = __builtin_amdgcn_exp2f(s[kb][8 * half + 2 * e2] - m_ref);
-            const float p1 = __builtin_amdgcn_exp2f(s[kb][8 * half + 2 * e2 + 1] - m_ref);
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * e2], a.c, neg_m));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * e2 + 1], a.c, neg_m));
             ls += p0 + p1;
             packed[e2] = TR::pack2(p0, p1);
           }
@@ -290,7 +299,7 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel_f32(FwdArgsF32 a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int h = lane >> 5;
   const int lr = lane & 31;
   const int N = a.N;
@@ -377,7 +386,7 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel_f32(FwdArgsF32 a) {
         float t = s[e] * a.c;
         if (need_mask) {
           const int key = k0 + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (key >= N || (CAUSAL && key > qrow)) t = -__builtin_inff();
+          t = (key >= N || (CAUSAL && key > qrow)) ? -__builtin_inff() : t;
         }
         s[e] = t;
         mx = fmaxf(mx, t);
@@ -442,8 +451,9 @@ hipError_t launch16(const FwdReq& r, hipStream_t st) {
   a.lse = r.lse;
   a.N = r.N;
   a.n_qtiles = (r.N + BR - 1) / BR;
-  a.c = fabsf(r.scale) * kLog2e;
+  a.c = r.scale == 0.f ? 1.f : fabsf(r.scale) * kLog2e;
   a.neg_mask = r.scale < 0.f ? 0x80008000u : 0u;
+  a.keep_mask = r.scale == 0.f ? 0u : 0xffffffffu;
   const long long nblk = (long long)r.B * r.H * a.n_qtiles;
   const dim3 grid((unsigned)nblk), block(BR / 32 * 64);
   if (r.causal)

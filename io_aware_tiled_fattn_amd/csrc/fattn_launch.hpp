@@ -43,6 +43,7 @@ bool fwd_tile_supported(int dtype, int d, int Br, int Bc);
 hipError_t launch_fwd(const FwdReq& r, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
-hipError_t launch_bwd(const BwdReq& r, hipStream_t stream);
+// stage: 0 = preprocess, 1 = dK/dV, 2 = dQ; -1 = all three in order
+hipError_t launch_bwd(const BwdReq& r, hipStream_t stream, int stage = -1);
 
 }  // namespace fattn

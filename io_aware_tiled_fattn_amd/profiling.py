@@ -1,0 +1,170 @@
+"""Summaries of rocprofv3 output for the attention kernels (kernel times and HBM traffic).
+
+Usage, after the three profiled runs of bench.py described in ``COMMANDS`` have written their
+CSV files under ``<run_dir>``::
+
+    python -m io_aware_tiled_fattn_amd.profiling <run_dir> <profiles_dir>
+
+writes ``kernel_times_<workload>.md``, ``hbm_traffic_<workload>.md`` and ``traffic.json`` into
+``profiles_dir``. HBM bytes come from the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch),
+each scaled by what the same counter reads for a plain elementwise copy of known size
+(256 MiB read + 256 MiB written) run in the same process. ``traffic.json`` records a hash of the
+kernel sources, so a reader can tell when the numbers no longer describe the built kernels.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+KERNEL_SOURCES = ("fattn_device.hpp", "fattn_fwd.hip", "fattn_bwd.hip")
+COPY_BYTES = 256 * 2**20  # the calibration copy reads and writes this many bytes each
+
+COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {run}/trace -o run -- "
+             "python -u bench.py --steps 10 --warmup 3 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {run}/fetch -o run -- "
+             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {run}/write -o run -- "
+             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy",
+}
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(kernel: str) -> str:
+    k = kernel.replace("fattn::(anonymous namespace)::", "").replace("fattn::", "")
+    k = k.replace("(unsigned short const*, unsigned short const*, float*, long long)", "")
+    k = k.replace("((anonymous namespace)::FwdArgs)", "").replace("((anonymous namespace)::BwdArgs)", "")
+    return k.replace("void ", "").strip()
+
+
+def _find(run_dir, sub, suffix):
+    d = os.path.join(run_dir, sub)
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def kernel_stats(run_dir):
+    rows = list(csv.DictReader(open(_find(run_dir, "trace", "kernel_stats.csv"))))
+    out = []
+    for r in rows:
+        out.append({"kernel": short_name(r["Name"]), "calls": int(r["Calls"]),
+                    "avg_us": float(r["AverageNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
+                    "max_us": float(r["MaxNs"]) / 1e3, "pct": float(r["Percentage"])})
+    return out
+
+
+def _counter_per_dispatch(path, counter):
+    per = collections.defaultdict(float)
+    meta = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        key = int(r["Dispatch_Id"])
+        per[key] += float(r["Counter_Value"])
+        meta[key] = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+    return per, meta
+
+
+def traffic(run_dir):
+    fetch, fmeta = _counter_per_dispatch(_find(run_dir, "fetch", "counter_collection.csv"), "FETCH_SIZE")
+    write, wmeta = _counter_per_dispatch(_find(run_dir, "write", "counter_collection.csv"), "WRITE_SIZE")
+
+    def calib(per, meta):
+        vals = [v for k, v in per.items() if "elementwise" in meta[k][0] and meta[k][1] == 128 * 2**20 // 8]
+        vals = [v for v in vals if v > 1000]
+        if not vals:
+            raise RuntimeError("calibration copy not found")
+        return (sum(vals) / len(vals)) * 1024 / COPY_BYTES  # counter bytes per true byte
+
+    fc, wc = calib(fetch, fmeta), calib(write, wmeta)
+    groups = collections.defaultdict(lambda: {"fetch": [], "write": []})
+    for k, v in fetch.items():
+        name, grid = fmeta[k]
+        if "elementwise" in name or "fill" in name.lower():
+            continue
+        groups[(name, grid)]["fetch"].append(v * 1024 / fc)
+    for k, v in write.items():
+        name, grid = wmeta[k]
+        if "elementwise" in name or "fill" in name.lower():
+            continue
+        groups[(name, grid)]["write"].append(v * 1024 / wc)
+    out = []
+    for (name, grid), g in sorted(groups.items()):
+        if not g["fetch"] or not g["write"]:
+            continue
+        out.append({"kernel": name, "grid": grid,
+                    "fetch_bytes": sum(g["fetch"]) / len(g["fetch"]),
+                    "write_bytes": sum(g["write"]) / len(g["write"])})
+    return out, fc, wc
+
+
+def write_summaries(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
+    os.makedirs(prof_dir, exist_ok=True)
+    stats = kernel_stats(run_dir)
+    cmd_note = "Commands (from the repository root, on the GPU box; RUN is an output folder):\n\n"
+    lines = [f"# Kernel times — bench.py step workload ({workload}) and the B=4 forward\n",
+             cmd_note + "    " + COMMANDS["trace"].format(run="RUN") + "\n",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for s in stats:
+        lines.append(f"| `{s['kernel']}` | {s['calls']} | {s['avg_us']:.1f} | {s['min_us']:.1f} | "
+                     f"{s['max_us']:.1f} | {s['pct']:.1f} |")
+    lines.append("\nThe forward kernel's calls mix the B=2 (step) and B=4 (prefill) workloads; "
+                 "bench.py times each live with HIP events.")
+    with open(os.path.join(prof_dir, f"kernel_times_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    tr, fc, wc = traffic(run_dir)
+    lines = [f"# HBM traffic per launch ({workload} and the B=4 forward)\n",
+             cmd_note + "    " + COMMANDS["fetch"].format(run="RUN") + "\n    " +
+             COMMANDS["write"].format(run="RUN") + "\n",
+             f"Calibration (elementwise copy, 256 MiB read + 256 MiB written): FETCH_SIZE reads "
+             f"{fc:.3f} x true bytes, WRITE_SIZE reads {wc:.3f} x; the figures below are divided by "
+             f"those factors.\n",
+             "| kernel | grid | fetched MiB | written MiB |", "|---|---|---|---|"]
+    for t in tr:
+        lines.append(f"| `{t['kernel']}` | {t['grid']} | {t['fetch_bytes'] / 2**20:.1f} | "
+                     f"{t['write_bytes'] / 2**20:.1f} |")
+    with open(os.path.join(prof_dir, f"hbm_traffic_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(prof_dir, "traffic.json"), "w") as f:
+        json.dump({"source_hash": source_hash(), "fetch_factor": fc, "write_factor": wc,
+                   "kernels": tr}, f, indent=1)
+    return stats, tr
+
+
+def load_traffic(prof_dir):
+    """Per-(kernel, grid) HBM bytes if they were measured on the current kernel sources."""
+    path = os.path.join(prof_dir, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("source_hash") != source_hash():
+        return None
+    return {(k["kernel"], k["grid"]): k for k in data["kernels"]}
+
+
+if __name__ == "__main__":
+    run = sys.argv[1]
+    prof = sys.argv[2] if len(sys.argv) > 2 else os.path.join(os.path.dirname(HERE), "profiles")
+    s, t = write_summaries(run, prof)
+    for x in s:
+        print(x)
+    for x in t:
+        print(x)

@@ -33,7 +33,8 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
     assert {"fattn_fwd", "fattn_fwd_tiled", "fattn_bwd", "fattn_bwd_workspace_size",
-            "fattn_strerror", "fattn_version"} <= set(names)
+            "fattn_strerror", "fattn_version", "fattn_bwd_preprocess", "fattn_bwd_dkdv",
+            "fattn_bwd_dq"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
         assert getattr(fa, n) is not None
@@ -112,3 +113,24 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros(1, 1, 8, 64)
     with pytest.raises(ValueError):
         fa.forward(q, q, q)
+
+
+@pytest.mark.parametrize("call,status", [
+    (lambda: fa.fattn_bwd_preprocess(None, P[1], P[2], 1, 1, 8, 64, 2), -1),
+    (lambda: fa.fattn_bwd_preprocess(P[0], P[1], P[2], 1, 1, 8, 64, 0), -4),
+    (lambda: fa.fattn_bwd_preprocess(P[0], P[1], P[0], 1, 1, 8, 64, 2), -11),
+    (lambda: fa.fattn_bwd_preprocess(P[0], P[1], MIS, 1, 1, 8, 64, 2), -6),
+    (lambda: fa.fattn_bwd_preprocess(P[0], P[1], P[2], 1, 1, 8, 96, 2), -3),
+    (lambda: fa.fattn_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], P[5], P[6], None, 1, 1, 8, 64, 0.1, 0, 2), -1),
+    (lambda: fa.fattn_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[6], 1, 1, 8, 64, 0.1, 0, 2), -11),
+    (lambda: fa.fattn_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[0], 1, 1, 8, 64, 0.1, 0, 2), -11),
+    (lambda: fa.fattn_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], 1, 1, 8, 64, float("nan"), 0, 2), -7),
+    (lambda: fa.fattn_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], 1, 1, 8, 64, 0.1, 5, 2), -12),
+    (lambda: fa.fattn_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], 1, 1, 8, 64, 0.1, 0, 0), -4),
+    (lambda: fa.fattn_bwd_dq(P[0], P[1], P[2], P[3], P[4], None, P[6], 1, 1, 8, 64, 0.1, 0, 2), -1),
+    (lambda: fa.fattn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], P[5], 1, 1, 8, 64, 0.1, 0, 2), -11),
+    (lambda: fa.fattn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], MIS, 1, 1, 8, 64, 0.1, 0, 2), -6),
+    (lambda: fa.fattn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 0, 1, 8, 64, 0.1, 0, 2), -2),
+])
+def test_backward_stages_reject_bad_arguments(L, call, status):
+    assert call() == status
