@@ -82,6 +82,51 @@ __device__ inline i16x4 lds_read_tr16(const void* p) {
 
 __device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// ---- direct global -> LDS loads (buffer_load_dwordx4 ... lds) --------------------------------
+// One instruction moves 16 bytes per lane from memory straight into LDS, without VGRPs: lane i's
+// 16 bytes land at LDS byte (lds + 16 * i), where lds is the same for the whole wave. The source
+// is the buffer resource's base + voffset (per lane) + soffset (scalar). Completion is tracked by
+// vmcnt; the caller waits with wait_vmcnt and then barriers before other waves read the data.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer (stride 0), num_records in bytes; out-of-range lanes read zeros
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ inline void buffer_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ inline void global_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Work-group barrier without the memory fence of __syncthreads (which would also wait for every
+// outstanding global->LDS prefetch). LDS reads of this wave are drained first, so no other wave
+// can overwrite a buffer this wave is still reading; prefetches stay in flight.
+__device__ inline void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// XOR swizzles of the 16-byte chunks of a row-major LDS tile (rows of D 16-bit elements), chosen
+// so that the reads below hit distinct banks:
+//  * K tiles are read with ds_read_b128, 32 consecutive rows at one chunk column per instruction;
+//  * V tiles are read with ds_read_b64_tr_b16, 64-byte column groups of 4 rows at a time, so the
+//    swizzle moves whole 4-chunk groups (it is a multiple of 4).
+template <int D>
+__device__ inline int swz_rowread(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+__device__ inline int swz_trread(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+
 // Block index remap so that consecutive logical blocks share an XCD: hardware dispatches block
 // ids round-robin over the 8 XCDs, so physical id x runs on XCD x % 8. When the grid is a
 // multiple of 8 the logical order visits, per XCD, one contiguous range of work.

@@ -9,22 +9,28 @@
 // visited (page 2, backward section and tips).
 //
 // gfx950 mapping (16-bit inputs):
-//  * a work-group of Br/32 waves; wave w owns query rows [q_base + 32w, +32).
+//  * a work-group of Br/32 waves; wave w owns query rows [q_base + 32w, +32). Two work-groups
+//    share a CU, so each SIMD runs two independent waves whose MFMA and VALU phases overlap.
 //  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: each lane then owns
 //    ONE query row (l % 32) and 16 keys per 32-key block, so the row max and row sum are
 //    in-register reductions plus one v_permlane32_swap between the two half-waves.
 //  * Q^T is the MFMA B operand, loaded once from HBM into registers; K is the A operand, read
-//    from a padded row-major LDS tile with ds_read_b128.
+//    from the LDS tile with ds_read_b128.
 //  * O^T = V^T P^T: P^T comes straight from the score accumulators (fp32 -> RNE 16-bit), V^T
 //    fragments come from the row-major V tile with ds_read_b64_tr_b16, so V is never transposed
 //    in memory. The MFMA reduction index is permuted consistently on both operands: slot s of
 //    half-wave h stands for key 16c + 4h + (s & 3) + 8 (s >> 2) of 16-key chunk c.
-//  * K/V tiles are double buffered in LDS; the next tile's global loads are issued before the
-//    current tile's math, one barrier per tile.
+//  * K/V tiles go from memory straight into LDS (buffer_load ... lds, no VGPR staging), two
+//    stages deep: the next tile's loads are issued right after the barrier that frees its stage
+//    and land while the current tile is computed. Tiles are stored unpadded with their 16-byte
+//    chunks XOR-swizzled per row, which keeps both read patterns free of bank conflicts.
 //  * The running max is kept in the log2 domain with scale*log2(e) folded into one multiply, and
 //    is only moved when a row's max grows by more than kRescaleSlack (2^8): the factor is then
 //    exactly 1 for almost every tile (page 2, tips), the exp2 arguments stay <= 8, and the result
 //    is unchanged because O and l always share the same reference max.
+//  * Work-group order: the 8 XCDs each take a contiguous range of heads; with the causal mask the
+//    query tiles of those heads run longest first (all heads' last tiles, then the ones before),
+//    which balances the triangular work across CUs.
 #include "fattn_device.hpp"
 #include "fattn_launch.hpp"
 
@@ -43,31 +49,57 @@ struct FwdArgs {
   float* lse;
   int N;
   int n_qtiles;
+  int bh_total;        // B * H
   float c;             // |scale| * log2(e), > 0
   uint32_t neg_mask;   // 0x80008000 flips the sign of two packed 16-bit Q elements (scale < 0)
   uint32_t keep_mask;  // 0 zeroes Q (scale == 0: every logit is 0), else all ones
 };
 
+// Block id -> (head, query tile). Hardware deals block ids round-robin over the 8 XCDs, so
+// block x runs on XCD x % 8; each XCD is given a contiguous range of heads.
+__device__ inline void fwd_block_coords(int bid, int nblocks, int n_qtiles, int bh_total, bool causal,
+                                        int* bh, int* qt) {
+  if ((bh_total & 7) == 0) {
+    const int hpx = bh_total >> 3;
+    const int xcd = bid & 7, local = bid >> 3;
+    if (causal) {
+      const int r = local / hpx;  // rank of the tile length, longest first
+      *bh = xcd * hpx + (local - r * hpx);
+      *qt = n_qtiles - 1 - r;
+    } else {
+      const int hh = local / n_qtiles;
+      *bh = xcd * hpx + hh;
+      *qt = local - hh * n_qtiles;
+    }
+    return;
+  }
+  const int logical = xcd_remap(bid, nblocks);
+  *bh = logical / n_qtiles;
+  *qt = logical - *bh * n_qtiles;
+  if (causal) *qt = n_qtiles - 1 - *qt;
+}
+
 template <int D, int BR, int BC>
 struct FwdCfg {
   static constexpr int NW = BR / 32;          // waves per work-group
   static constexpr int NT = NW * 64;          // threads per work-group
-  static constexpr int KSTR = D + 8;          // K tile row pitch in LDS (elements)
-  static constexpr int VSTR = D + 16;         // V tile row pitch in LDS (elements)
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
-  static constexpr int CH = BC * CPR / NT;    // chunks per thread per tensor per tile
-  static constexpr int KBUF = BC * KSTR;
-  static constexpr int STAGE = KBUF + BC * VSTR;
-  static constexpr int LDS_ELEMS = 2 * STAGE;
+  static constexpr int LPT = BC * CPR / NT;   // 16-byte loads per thread per tile per tensor
+  static constexpr int TILE_B = BC * D * 2;   // bytes of one K (or V) tile
+  static constexpr int STAGE_B = 2 * TILE_B;  // K then V
+  static constexpr int LDS_B = 2 * STAGE_B;   // two stages
   static_assert(BC * CPR % NT == 0, "tile load split");
   static_assert(BR % 32 == 0 && BC % 32 == 0 && D % 32 == 0, "tile shape");
 };
 
-template <typename TR, int D, int BR, int BC, bool CAUSAL>
+// BIG: the head's K/V exceed the 32-bit range of buffer offsets, so tiles are fetched with
+// per-lane 64-bit global addresses instead.
+template <typename TR, int D, int BR, int BC, bool CAUSAL, bool BIG>
 __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   using Cfg = FwdCfg<D, BR, BC>;
   using vec8 = typename TR::vec8;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[Cfg::LDS_ELEMS];
+  constexpr int NT = Cfg::NT, CPR = Cfg::CPR, LPT = Cfg::LPT, TILE_B = Cfg::TILE_B;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS_B];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -76,11 +108,8 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   const int lr = lane & 31;
   const int N = a.N;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / a.n_qtiles;
-  int qt = logical - bh * a.n_qtiles;
-  if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest rows first
-
+  int bh, qt;
+  fwd_block_coords(blockIdx.x, gridDim.x, a.n_qtiles, a.bh_total, CAUSAL, &bh, &qt);
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* __restrict__ Qh = a.q + head;
   const uint16_t* __restrict__ Kh = a.k + head;
@@ -106,33 +135,40 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   const int kv_end = CAUSAL ? min(N, q_base + BR) : N;
   const int n_kv = (kv_end + BC - 1) / BC;
 
-  u32x4 kr[Cfg::CH], vr[Cfg::CH];
-  auto load_tile = [&](int j) {
+  // Load i of this thread fills LDS chunk i*NT + tid of a tile: row r = chunk / CPR holds, at
+  // chunk position p = chunk % CPR, the source chunk p ^ swizzle(r).
+  uint32_t offK[LPT], offV[LPT];  // byte offsets within a tile: row * 2D + source chunk * 16
+  int drow[LPT];
 #pragma unroll
-    for (int i = 0; i < Cfg::CH; ++i) {
-      const int c = tid + i * Cfg::NT;
-      const int row = c / Cfg::CPR;
-      const int col = c % Cfg::CPR;
-      const int key = j * BC + row;
-      if (key < N) {
-        kr[i] = *(const u32x4*)(Kh + (size_t)key * D + col * 8);
-        vr[i] = *(const u32x4*)(Vh + (size_t)key * D + col * 8);
-      } else {
-        kr[i] = u32x4{0u, 0u, 0u, 0u};
-        vr[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < LPT; ++i) {
+    const int chunk = i * NT + tid;
+    const int row = chunk / CPR, pos = chunk % CPR;
+    drow[i] = row;
+    offK[i] = (uint32_t)(row * D * 2 + (pos ^ swz_rowread<D>(row)) * 16);
+    offV[i] = (uint32_t)(row * D * 2 + (pos ^ swz_trread<D>(row)) * 16);
+  }
+  const uint32_t head_bytes = BIG ? 0u : (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(Kh, head_bytes);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(Vh, head_bytes);
+  auto issue = [&](int j) {
+    uint8_t* st = smem + (j & 1) * Cfg::STAGE_B + w * 64 * 16;
+    if (!BIG && (j + 1) * BC <= N) {
+      const uint32_t soff = (uint32_t)(j * BC) * (D * 2);
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        buffer_lds16(rK, st + i * NT * 16, offK[i], soff);
+        buffer_lds16(rV, st + TILE_B + i * NT * 16, offV[i], soff);
       }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* Ks = smem + buf * Cfg::STAGE;
-    uint16_t* Vs = Ks + Cfg::KBUF;
+    } else {
+      // ragged last tile (or a huge head): rows past the end repeat row N - 1, so every LDS row
+      // holds real, finite data; those keys are masked below
 #pragma unroll
-    for (int i = 0; i < Cfg::CH; ++i) {
-      const int c = tid + i * Cfg::NT;
-      const int row = c / Cfg::CPR;
-      const int col = c % Cfg::CPR;
-      *(u32x4*)(Ks + row * Cfg::KSTR + col * 8) = kr[i];
-      *(u32x4*)(Vs + row * Cfg::VSTR + col * 8) = vr[i];
+      for (int i = 0; i < LPT; ++i) {
+        const size_t src_row = (size_t)min(j * BC + drow[i], N - 1) * (D * 2);
+        const uint32_t in_row = (uint32_t)(drow[i] * D * 2);
+        global_lds16((const uint8_t*)Kh + src_row + (offK[i] - in_row), st + i * NT * 16);
+        global_lds16((const uint8_t*)Vh + src_row + (offV[i] - in_row), st + TILE_B + i * NT * 16);
+      }
     }
   };
 
@@ -144,102 +180,111 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   float m_ref = -__builtin_inff();
   float l_part = 0.f;
 
-  load_tile(0);
-  store_tile(0);
+  const int tr_row = 4 * h + ((lane & 15) >> 2);
+  const int tr_colb = (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;  // byte offset in a 64-B group
+
+  issue(0);
   for (int j = 0; j < n_kv; ++j) {
-    if (j + 1 < n_kv) load_tile(j + 1);
-    __syncthreads();
+    wait_vmcnt<0>();  // this wave's loads of tile j have landed
+    barrier_lds();    // ... and everyone's; stage (j + 1) & 1 is no longer being read
+    if (j + 1 < n_kv) issue(j + 1);
     const int k0 = j * BC;
-    if (wave_active && k0 < wave_kv_end) {
-      const uint16_t* Ks = smem + (j & 1) * Cfg::STAGE;
-      const uint16_t* Vs = Ks + Cfg::KBUF;
+    if (!(wave_active && k0 < wave_kv_end)) continue;
+    const uint8_t* Ks = smem + (j & 1) * Cfg::STAGE_B;
+    const uint8_t* Vs = Ks + TILE_B;
 
-      // S^T = K Q^T for BC/32 blocks of 32 keys.
-      // (the BC/32 accumulators are independent chains, interleaved step by step)
-      f32x16 s[BC / 32];
+    // S^T = K Q^T for BC/32 blocks of 32 keys; the BC/32 accumulators are independent chains.
+    f32x16 s[BC / 32];
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
+    for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st)
+    for (int st = 0; st < D / 16; ++st)
 #pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb) {
-          const vec8 kf = *(const vec8*)(Ks + (kb * 32 + lr) * Cfg::KSTR + 16 * st + 8 * h);
-          s[kb] = TR::mma(kf, qf[st], s[kb]);
-        }
-
-      // Mask (diagonal and ragged tiles only), then the row max of the raw scores.
-      const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
-      if (need_mask) {
-        // element (kb, e) holds key k0 + kb*32 + 8(e>>2) + 4h + (e&3); it is masked when that
-        // relative index exceeds lim
-        int lim = N - 1 - k0;
-        if (CAUSAL) lim = min(lim, qrow - k0);
-        lim -= 4 * h;
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            s[kb][e] = (kb * 32 + 8 * (e >> 2) + (e & 3) > lim) ? -__builtin_inff() : s[kb][e];
+      for (int kb = 0; kb < BC / 32; ++kb) {
+        const int row = kb * 32 + lr;
+        const vec8 kf = *(const vec8*)(Ks + row * (D * 2) + (((2 * st + h) ^ swz_rowread<D>(row)) * 16));
+        s[kb] = TR::mma(kf, qf[st], s[kb]);
       }
-      float mx = -__builtin_inff();
+    // keep the K fragment reads one step ahead of the MFMAs that consume them
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (BC / 32), 0);
+#pragma unroll
+    for (int st = 0; st < D / 16 - 2; ++st) {
+      __builtin_amdgcn_sched_group_barrier(0x008, BC / 32, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, BC / 32, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * (BC / 32), 0);
+
+    // Mask (diagonal and ragged tiles only), then the row max of the raw scores.
+    const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
+    if (need_mask) {
+      // element (kb, e) holds key k0 + kb*32 + 8(e>>2) + 4h + (e&3); it is masked when that
+      // relative index exceeds lim
+      int lim = N - 1 - k0;
+      if (CAUSAL) lim = min(lim, qrow - k0);
+      lim -= 4 * h;
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-      mx = max_halves(mx) * a.c;  // c > 0, so this is the max of the log2-domain logits
+        for (int e = 0; e < 16; ++e)
+          s[kb][e] = (kb * 32 + 8 * (e >> 2) + (e & 3) > lim) ? -__builtin_inff() : s[kb][e];
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+    mx = max_halves(mx) * a.c;  // c > 0, so this is the max of the log2-domain logits
 
-      // Move the reference max only when it grew by more than the slack.
-      const float m_new = fmaxf(m_ref, mx);
-      const bool grow = m_new > m_ref + kRescaleSlack;
-      if (wave_any(grow)) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
-        if (grow) m_ref = m_new;
-        l_part *= alpha;
+    // Move the reference max only when it grew by more than the slack.
+    const float m_new = fmaxf(m_ref, mx);
+    const bool grow = m_new > m_ref + kRescaleSlack;
+    if (wave_any(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+      if (grow) m_ref = m_new;
+      l_part *= alpha;
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b)
+      for (int b = 0; b < D / 32; ++b)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
+        for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
+    }
+
+    // P^T = exp2(s*c - m_ref) (masked scores are -inf and give 0), packed to 16-bit MFMA B
+    // fragments (8 keys per 16-key chunk).
+    const float neg_m = -m_ref;
+    vec8 pf[BC / 16];
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 packed;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * e2], a.c, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * e2 + 1], a.c, neg_m));
+          ls += p0 + p1;
+          packed[e2] = TR::pack2(p0, p1);
+        }
+        pf[2 * kb + half] = bitcast<vec8>(packed);
       }
+    l_part += ls;
 
-      // P^T = exp2(s*c - m_ref) (masked scores are -inf and give 0), packed to 16-bit MFMA B
-      // fragments (8 keys per 16-key chunk).
-      const float neg_m = -m_ref;
-      vec8 pf[BC / 16];
-      float ls = 0.f;
+    // O^T += V^T P^T; V^T fragments via the transposed LDS read (rows 16c + tr_row and +8).
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
+    for (int c = 0; c < BC / 16; ++c) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          u32x4 packed;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * e2], a.c, neg_m));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * e2 + 1], a.c, neg_m));
-            ls += p0 + p1;
-            packed[e2] = TR::pack2(p0, p1);
-          }
-          pf[2 * kb + half] = bitcast<vec8>(packed);
-        }
-      l_part += ls;
-
-      // O^T += V^T P^T; V^T fragments via the transposed LDS read.
-      const int tr_row = 4 * h + ((lane & 15) >> 2);
-      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-      for (int c = 0; c < BC / 16; ++c) {
-#pragma unroll
-        for (int b = 0; b < D / 32; ++b) {
-          const uint16_t* p0 = Vs + (16 * c + tr_row) * Cfg::VSTR + 32 * b + tr_col;
-          const i16x4 lo = lds_read_tr16(p0);
-          const i16x4 hi = lds_read_tr16(p0 + 8 * Cfg::VSTR);
-          const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[b] = TR::mma(bitcast<vec8>(both), pf[c], acc[b]);
-        }
+      for (int b = 0; b < D / 32; ++b) {
+        const int r0 = 16 * c + tr_row, r1 = r0 + 8;
+        const uint8_t* p0 = Vs + r0 * (D * 2) + (((4 * b) ^ swz_trread<D>(r0)) * 16) + tr_colb;
+        const uint8_t* p1 = Vs + r1 * (D * 2) + (((4 * b) ^ swz_trread<D>(r1)) * 16) + tr_colb;
+        const i16x4 lo = lds_read_tr16(p0);
+        const i16x4 hi = lds_read_tr16(p1);
+        const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[b] = TR::mma(bitcast<vec8>(both), pf[c], acc[b]);
       }
     }
-    if (j + 1 < n_kv) store_tile((j + 1) & 1);
   }
 
   if (!wave_active) return;
@@ -451,15 +496,21 @@ hipError_t launch16(const FwdReq& r, hipStream_t st) {
   a.lse = r.lse;
   a.N = r.N;
   a.n_qtiles = (r.N + BR - 1) / BR;
+  a.bh_total = r.B * r.H;
   a.c = r.scale == 0.f ? 1.f : fabsf(r.scale) * kLog2e;
   a.neg_mask = r.scale < 0.f ? 0x80008000u : 0u;
   a.keep_mask = r.scale == 0.f ? 0u : 0xffffffffu;
   const long long nblk = (long long)r.B * r.H * a.n_qtiles;
   const dim3 grid((unsigned)nblk), block(BR / 32 * 64);
-  if (r.causal)
-    hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, true>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, false>), grid, block, 0, st, a);
+  // buffer offsets are 32-bit: heads of 2 GiB or more take the 64-bit address path
+  const bool big = (size_t)r.N * D * 2 >= ((size_t)1 << 31);
+  if (r.causal) {
+    if (big) hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, true, false>), grid, block, 0, st, a);
+  } else {
+    if (big) hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, false, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
