@@ -11,12 +11,12 @@
 //
 // Three kernels, all in stream order:
 //  1. bwd_pre:   D = rowsum(dO * O) (float32 workspace), one pass over O and dO.
-//  2. bwd_dkdv:  one work-group per (b*h, 128-key tile); each of its 4 waves keeps 32 keys of K
-//               and V in registers and the float32 dK, dV accumulators, while Q, dO tiles of 64
-//               queries stream through double-buffered LDS. Scores are formed as S = Q K^T so
-//               that every lane owns ONE key: P and dS then serve directly as the MFMA A
-//               operand of dV += P^T dO and dK += dS^T Q, whose B operands (dO and Q with the
-//               query index as reduction index) come from the row-major LDS tiles through
+//  2. bwd_dkdv:  one work-group per (b*h, 128-key tile), in two passes (dV, then dK); each of
+//               its 4 waves keeps 32 keys of K (and V) in registers and a float32 accumulator,
+//               while Q, dO tiles of 64 queries stream memory -> LDS, two stages deep. Scores are
+//               formed as S = Q K^T so that every lane owns ONE key: P and dS then serve directly
+//               as the MFMA A operand of dV += P^T dO and dK += dS^T Q, whose B operands (dO and
+//               Q with the query index as reduction index) come from the same LDS tiles through
 //               ds_read_b64_tr_b16.
 //  3. bwd_dq:    one work-group per (b*h, 128-query tile), the forward's layout: S^T = K Q^T and
 //               dP^T = V dO^T give each lane ONE query (its LSE and D are per-lane scalars);
@@ -43,6 +43,7 @@ struct BwdArgs {
   const float* dvec;
   int N;
   int ntiles;   // tiles per head along the grid's sequence axis
+  int bh_total; // B * H
   float c;      // scale * log2(e) (signed)
   float scale;  // signed softmax scale
 };
@@ -80,28 +81,82 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------------------------
+// Shared by the two matmul kernels.
+
+// Block id -> (head, tile along the grid's sequence axis). Each of the 8 XCDs (block x runs on
+// XCD x % 8) takes a contiguous range of heads. With the causal mask the tiles with the most work
+// run first across all heads of an XCD: for dK/dV that is the first key tile (it sees every query
+// tile), for dQ the last query tile.
+__device__ inline void bwd_block_coords(int bid, int nblocks, int ntiles, int bh_total, bool causal,
+                                        bool long_is_low, int* bh, int* t) {
+  if ((bh_total & 7) == 0) {
+    const int hpx = bh_total >> 3;
+    const int xcd = bid & 7, local = bid >> 3;
+    if (causal) {
+      const int r = local / hpx;
+      *bh = xcd * hpx + (local - r * hpx);
+      *t = long_is_low ? r : ntiles - 1 - r;
+    } else {
+      const int hh = local / ntiles;
+      *bh = xcd * hpx + hh;
+      *t = local - hh * ntiles;
+    }
+    return;
+  }
+  const int logical = xcd_remap(bid, nblocks);
+  *bh = logical / ntiles;
+  *t = logical - *bh * ntiles;
+  if (causal && !long_is_low) *t = ntiles - 1 - *t;
+}
+
+// Byte address, inside a tile swizzled with swz_dual, of the 8 bytes this lane contributes to a
+// ds_read_b64_tr_b16: row R, 16-bit element column E (a multiple of 4).
+template <int D>
+__device__ inline int tr_read_addr(int R, int E) {
+  return R * (D * 2) + (((E >> 3) ^ swz_dual<D>(R)) << 4) + ((E & 7) << 1);
+}
+// Byte address of the 16-byte chunk c of row R in a tile swizzled with swz_dual.
+template <int D>
+__device__ inline int row_read_addr(int R, int c) {
+  return R * (D * 2) + ((c ^ swz_dual<D>(R)) << 4);
+}
+
+// ---------------------------------------------------------------------------------------------
 // 2. dK, dV.
+//
+// One work-group per (b*h, 128-key tile); each of its 4 waves keeps 32 keys of K and V in
+// registers (MFMA B operands) and the float32 dK, dV accumulators. Tiles of 64 queries of Q and dO
+// go from memory straight into LDS (two stages), with the per-row log2-domain LSE and D beside
+// them. S = Q K^T and dP = dO V^T put ONE key in each lane, so P and dS serve directly as the A
+// operand of dV += P^T dO and dK += dS^T Q, whose B operands (dO and Q with the query index as
+// reduction index) come from the same LDS tiles through ds_read_b64_tr_b16.
 
 template <int D>
 struct DkdvCfg {
-  static constexpr int BKV = 128;            // keys per work-group (32 per wave)
-  static constexpr int BQ = 64;              // queries per step
+  static constexpr int BKV = 128;               // keys per work-group (32 per wave)
+  static constexpr int BQ = 64;                 // queries per step
   static constexpr int NT = 256;
-  static constexpr int STR = D + 8;          // LDS row pitch of the Q and dO tiles (elements)
   static constexpr int CPR = D / 8;
-  static constexpr int CH = BQ * CPR / NT;   // 16-byte chunks per thread per tensor per step
-  static constexpr int TILE = BQ * STR;      // elements of one Q (or dO) tile
-  static constexpr int STAGE_E = 2 * TILE;   // Q + dO
+  static constexpr int LPT = BQ * CPR / NT;     // 16-byte loads per thread per tile per tensor
+  static constexpr int TILE_B = BQ * D * 2;     // bytes of one Q (or dO) tile
+  static constexpr int ROWS_B = 2 * BQ * 4;     // LSE (log2 domain) then D, float32
+  static constexpr int STAGE_B = 2 * TILE_B + ROWS_B;
   static_assert(BQ * CPR % NT == 0, "tile split");
 };
 
-template <typename TR, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+// MODE 1 accumulates dV only (S, P, dV += P^T dO: 2 GEMMs), MODE 2 dK only (S, dP, dS,
+// dK += dS^T Q: 3 GEMMs). The two passes recompute S, one GEMM more than a fused pass, but each
+// holds half the accumulators: both fit in 256 registers, so two waves share every SIMD and their
+// MFMA and VALU work overlaps (a fused pass needs ~300 registers and runs one wave per SIMD).
+template <typename TR, int D, bool CAUSAL, bool BIG, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(BwdArgs a) {
+  static_assert(MODE == 1 || MODE == 2, "dV pass or dK pass");
+  constexpr bool DO_DV = MODE == 1, DO_DK = MODE == 2;
   using Cfg = DkdvCfg<D>;
   using vec8 = typename TR::vec8;
-  constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::STAGE_E];
-  __shared__ __attribute__((aligned(16))) float srow[2][2][BQ];  // [stage][lse2 | D][query]
+  constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, NT = Cfg::NT, CPR = Cfg::CPR, LPT = Cfg::LPT;
+  constexpr int TILE_B = Cfg::TILE_B;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * Cfg::STAGE_B];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -110,9 +165,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int lr = lane & 31;
   const int N = a.N;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / a.ntiles;
-  const int jt = logical - bh * a.ntiles;  // causal: low tiles see the most queries, so go first
+  int bh, jt;
+  bwd_block_coords(blockIdx.x, gridDim.x, a.ntiles, a.bh_total, CAUSAL, true, &bh, &jt);
   const size_t head = (size_t)bh * (size_t)N * D;
   const size_t rowbase = (size_t)bh * (size_t)N;
   const uint16_t* __restrict__ Qh = a.q + head;
@@ -147,68 +201,82 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int n_qt = (N + BQ - 1) / BQ;
   const int i_begin = CAUSAL ? (jt * BKV) / BQ : 0;
 
-  u32x4 qr[Cfg::CH], dr[Cfg::CH];
-  float lr2 = 0.f, dvr = 0.f;
-  auto load_tile = [&](int i) {
+  // Load i of this thread fills LDS chunk i*NT + tid of a Q (dO) tile with the source chunk
+  // (chunk % CPR) ^ swz_dual(row) of row chunk / CPR.
+  uint32_t off[LPT];
+  int drow[LPT];
 #pragma unroll
-    for (int t = 0; t < Cfg::CH; ++t) {
-      const int c = tid + t * Cfg::NT;
-      const int row = c / Cfg::CPR;
-      const int col = c % Cfg::CPR;
-      const int q = i * BQ + row;
-      if (q < N) {
-        qr[t] = *(const u32x4*)(Qh + (size_t)q * D + col * 8);
-        dr[t] = *(const u32x4*)(dOh + (size_t)q * D + col * 8);
-      } else {
-        qr[t] = u32x4{0u, 0u, 0u, 0u};
-        dr[t] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < LPT; ++i) {
+    const int chunk = i * NT + tid;
+    const int row = chunk / CPR, pos = chunk % CPR;
+    drow[i] = row;
+    off[i] = (uint32_t)(row * D * 2 + (pos ^ swz_dual<D>(row)) * 16);
+  }
+  const uint32_t head_bytes = BIG ? 0u : (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Qh, head_bytes);
+  const __amdgpu_buffer_rsrc_t rdO = make_rsrc(dOh, head_bytes);
+  auto issue = [&](int i) {
+    uint8_t* st = smem + (i & 1) * Cfg::STAGE_B + w * 64 * 16;
+    if (!BIG && (i + 1) * BQ <= N) {
+      const uint32_t soff = (uint32_t)(i * BQ) * (D * 2);
+#pragma unroll
+      for (int t = 0; t < LPT; ++t) {
+        buffer_lds16(rQ, st + t * NT * 16, off[t], soff);
+        buffer_lds16(rdO, st + TILE_B + t * NT * 16, off[t], soff);
+      }
+    } else {
+      // ragged last tile (or a huge head): rows past the end repeat row N - 1; their P and dS
+      // are zeroed below, so they add nothing
+#pragma unroll
+      for (int t = 0; t < LPT; ++t) {
+        const size_t src_row = (size_t)min(i * BQ + drow[t], N - 1) * (D * 2);
+        const uint32_t in_row = off[t] - (uint32_t)(drow[t] * D * 2);
+        global_lds16((const uint8_t*)Qh + src_row + in_row, st + t * NT * 16);
+        global_lds16((const uint8_t*)dOh + src_row + in_row, st + TILE_B + t * NT * 16);
       }
     }
+  };
+  // per-query LSE (log2 domain) and D of tile i: loaded into registers, stored after the compute
+  float lr2 = 0.f, dvr = 0.f;
+  auto load_rows = [&](int i) {
     if (tid < BQ) {
-      const int q = i * BQ + tid;
-      // rows past the end get LSE = +inf, so their P is exactly 0
-      lr2 = q < N ? a.lse[rowbase + q] * kLog2e : __builtin_inff();
-      dvr = q < N ? a.dvec[rowbase + q] : 0.f;
+      const int q = min(i * BQ + tid, N - 1);
+      lr2 = a.lse[rowbase + q] * kLog2e;
+      dvr = a.dvec[rowbase + q];
     }
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* Qs = smem + buf * Cfg::STAGE_E;
-    uint16_t* dOs = Qs + Cfg::TILE;
-#pragma unroll
-    for (int t = 0; t < Cfg::CH; ++t) {
-      const int c = tid + t * Cfg::NT;
-      const int row = c / Cfg::CPR;
-      const int col = c % Cfg::CPR;
-      *(u32x4*)(Qs + row * Cfg::STR + col * 8) = qr[t];
-      *(u32x4*)(dOs + row * Cfg::STR + col * 8) = dr[t];
-    }
+  auto store_rows = [&](int i) {
     if (tid < BQ) {
-      srow[buf][0][tid] = lr2;
-      srow[buf][1][tid] = dvr;
+      float* rows = (float*)(smem + (i & 1) * Cfg::STAGE_B + 2 * TILE_B);
+      rows[tid] = lr2;
+      rows[BQ + tid] = dvr;
     }
   };
 
+  // transposed-read coordinates: rows 16c + tr_row (+8), element column 32b + tr_col
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   if (i_begin < n_qt) {
-    load_tile(i_begin);
-    store_tile(0);
+    load_rows(i_begin);
+    issue(i_begin);
+    store_rows(i_begin);
   }
   for (int i = i_begin; i < n_qt; ++i) {
-    const int buf = (i - i_begin) & 1;
-    if (i + 1 < n_qt) load_tile(i + 1);
-    __syncthreads();
+    wait_vmcnt<0>();
+    barrier_lds();
+    if (i + 1 < n_qt) {
+      load_rows(i + 1);  // plain loads first, so waiting for them does not wait for the tiles
+      issue(i + 1);
+    }
     const int q_base = i * BQ;
     // causal: the whole tile lies above this wave's keys -> P = 0, nothing to add
     if (wave_active && !(CAUSAL && q_base + BQ - 1 < key0)) {
-      const uint16_t* Qs = smem + buf * Cfg::STAGE_E;
-      const uint16_t* dOs = Qs + Cfg::TILE;
-      const float* lse2s = srow[buf][0];
-      const float* dvs = srow[buf][1];
-
-      vec8 pp[BQ / 16], dsp[BQ / 16];
-      const bool need_mask = CAUSAL && key0 + 31 > q_base;
+      const uint8_t* Qs = smem + (i & 1) * Cfg::STAGE_B;
+      const uint8_t* dOs = Qs + TILE_B;
+      const float* lse2s = (const float*)(Qs + 2 * TILE_B);
+      const float* dvs = lse2s + BQ;
+      const bool need_mask = (CAUSAL && key0 + 31 > q_base) || (q_base + BQ > N);
 #pragma unroll
       for (int qb = 0; qb < BQ / 32; ++qb) {
         f32x16 s, dp;
@@ -219,10 +287,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {  // two independent chains, interleaved
-          const vec8 qa = *(const vec8*)(Qs + (qb * 32 + lr) * Cfg::STR + 16 * st + 8 * h);
-          const vec8 da = *(const vec8*)(dOs + (qb * 32 + lr) * Cfg::STR + 16 * st + 8 * h);
+          const int addr = row_read_addr<D>(qb * 32 + lr, 2 * st + h);
+          const vec8 qa = *(const vec8*)(Qs + addr);
+          const vec8 da = *(const vec8*)(dOs + addr);
           s = TR::mma(qa, kf[st], s);
-          dp = TR::mma(da, vf[st], dp);
+          if (DO_DK) dp = TR::mma(da, vf[st], dp);
         }
         // element 4j + r is query qb*32 + 8j + 4h + r of the tile, key = this lane's key
         float p[16], ds[16];
@@ -234,11 +303,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           for (int r = 0; r < 4; ++r) {
             const int e = 4 * j + r;
             float pv = __builtin_amdgcn_exp2f(fmaf(s[e], a.c, -l4[r]));
-            if (need_mask) pv = (key > q_base + qb * 32 + 8 * j + 4 * h + r) ? 0.f : pv;
+            if (need_mask) {
+              const int qq = q_base + qb * 32 + 8 * j + 4 * h + r;
+              pv = ((CAUSAL && key > qq) || qq >= N) ? 0.f : pv;
+            }
             p[e] = pv;
             ds[e] = pv * (dp[e] - d4[r]);
           }
         }
+        vec8 pp[2], dsp[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           u32x4 pu, du;
@@ -247,28 +320,35 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
             pu[e2] = TR::pack2(p[8 * half + 2 * e2], p[8 * half + 2 * e2 + 1]);
             du[e2] = TR::pack2(ds[8 * half + 2 * e2], ds[8 * half + 2 * e2 + 1]);
           }
-          pp[2 * qb + half] = bitcast<vec8>(pu);
-          dsp[2 * qb + half] = bitcast<vec8>(du);
+          pp[half] = bitcast<vec8>(pu);
+          dsp[half] = bitcast<vec8>(du);
         }
-      }
-      // dV += P^T dO and dK += dS^T Q; B operands via the transposed LDS read.
+        // dV += P^T dO and dK += dS^T Q over this block's two 16-query chunks; B operands via
+        // the transposed LDS read.
 #pragma unroll
-      for (int c = 0; c < BQ / 16; ++c) {
+        for (int half = 0; half < 2; ++half) {
+          const int c = 2 * qb + half;
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b) {
-          const int off = (16 * c + tr_row) * Cfg::STR + 32 * b + tr_col;
-          const i16x4 d0 = lds_read_tr16(dOs + off);
-          const i16x4 d1 = lds_read_tr16(dOs + off + 8 * Cfg::STR);
-          const i16x8 dd = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-          adv[b] = TR::mma(pp[c], bitcast<vec8>(dd), adv[b]);
-          const i16x4 q0 = lds_read_tr16(Qs + off);
-          const i16x4 q1 = lds_read_tr16(Qs + off + 8 * Cfg::STR);
-          const i16x8 qq = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-          adk[b] = TR::mma(dsp[c], bitcast<vec8>(qq), adk[b]);
+          for (int b = 0; b < D / 32; ++b) {
+            const int a0 = tr_read_addr<D>(16 * c + tr_row, 32 * b + tr_col);
+            const int a1 = tr_read_addr<D>(16 * c + tr_row + 8, 32 * b + tr_col);
+            if (DO_DV) {
+              const i16x4 d0 = lds_read_tr16(dOs + a0);
+              const i16x4 d1 = lds_read_tr16(dOs + a1);
+              const i16x8 dd = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+              adv[b] = TR::mma(pp[half], bitcast<vec8>(dd), adv[b]);
+            }
+            if (DO_DK) {
+              const i16x4 q0 = lds_read_tr16(Qs + a0);
+              const i16x4 q1 = lds_read_tr16(Qs + a1);
+              const i16x8 qq = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+              adk[b] = TR::mma(dsp[half], bitcast<vec8>(qq), adk[b]);
+            }
+          }
         }
       }
     }
-    if (i + 1 < n_qt) store_tile(buf ^ 1);
+    if (i + 1 < n_qt) store_rows(i + 1);
   }
 
   if (!wave_active) return;
@@ -282,8 +362,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int b = 0; b < D / 32; ++b) {
           const size_t idx = head + (size_t)kk * D + 32 * b + lr;
-          a.dk[idx] = __builtin_bit_cast(uint16_t, TR::from_f32(adk[b][4 * j + r] * a.scale));
-          a.dv[idx] = __builtin_bit_cast(uint16_t, TR::from_f32(adv[b][4 * j + r]));
+          if (DO_DK) a.dk[idx] = __builtin_bit_cast(uint16_t, TR::from_f32(adk[b][4 * j + r] * a.scale));
+          if (DO_DV) a.dv[idx] = __builtin_bit_cast(uint16_t, TR::from_f32(adv[b][4 * j + r]));
         }
       }
     }
@@ -291,27 +371,31 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // 3. dQ.
+//
+// One work-group per (b*h, 128-query tile), the forward's layout: S^T = K Q^T and dP^T = V dO^T
+// give each lane ONE query (its LSE and D are per-lane scalars); dQ^T += K^T dS^T takes K^T from
+// the K tile through the transposed read. K and V tiles of 64 keys stream memory -> LDS, two
+// stages deep.
 
 template <int D>
 struct DqCfg {
-  static constexpr int BQ = 128;           // queries per work-group (32 per wave)
-  static constexpr int BK = 64;            // keys per step
+  static constexpr int BQ = 128;              // queries per work-group (32 per wave)
+  static constexpr int BK = 64;               // keys per step
   static constexpr int NT = 256;
-  static constexpr int KSTR = D + 8;
-  static constexpr int VSTR = D + 8;
   static constexpr int CPR = D / 8;
-  static constexpr int CH = BK * CPR / NT;
-  static constexpr int KBUF = BK * KSTR;
-  static constexpr int STAGE = KBUF + BK * VSTR;
+  static constexpr int LPT = BK * CPR / NT;
+  static constexpr int TILE_B = BK * D * 2;
+  static constexpr int STAGE_B = 2 * TILE_B;  // K then V
   static_assert(BK * CPR % NT == 0, "tile split");
 };
 
-template <typename TR, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+template <typename TR, int D, bool CAUSAL, bool BIG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BwdArgs a) {
   using Cfg = DqCfg<D>;
   using vec8 = typename TR::vec8;
-  constexpr int BQ = Cfg::BQ, BK = Cfg::BK;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::STAGE];
+  constexpr int BQ = Cfg::BQ, BK = Cfg::BK, NT = Cfg::NT, CPR = Cfg::CPR, LPT = Cfg::LPT;
+  constexpr int TILE_B = Cfg::TILE_B;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * Cfg::STAGE_B];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -320,10 +404,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int lr = lane & 31;
   const int N = a.N;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / a.ntiles;
-  int qt = logical - bh * a.ntiles;
-  if (CAUSAL) qt = a.ntiles - 1 - qt;
+  int bh, qt;
+  bwd_block_coords(blockIdx.x, gridDim.x, a.ntiles, a.bh_total, CAUSAL, false, &bh, &qt);
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* __restrict__ Kh = a.k + head;
   const uint16_t* __restrict__ Vh = a.v + head;
@@ -358,101 +440,104 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int kv_end = CAUSAL ? min(N, q_base + BQ) : N;
   const int n_kv = (kv_end + BK - 1) / BK;
 
-  u32x4 kr[Cfg::CH], vr[Cfg::CH];
-  auto load_tile = [&](int j) {
+  // K tiles are read both row-wise and transposed (swz_dual); V tiles only row-wise.
+  uint32_t offK[LPT], offV[LPT];
+  int drow[LPT];
 #pragma unroll
-    for (int i = 0; i < Cfg::CH; ++i) {
-      const int c = tid + i * Cfg::NT;
-      const int row = c / Cfg::CPR;
-      const int col = c % Cfg::CPR;
-      const int kk = j * BK + row;
-      if (kk < N) {
-        kr[i] = *(const u32x4*)(Kh + (size_t)kk * D + col * 8);
-        vr[i] = *(const u32x4*)(Vh + (size_t)kk * D + col * 8);
-      } else {
-        kr[i] = u32x4{0u, 0u, 0u, 0u};
-        vr[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < LPT; ++i) {
+    const int chunk = i * NT + tid;
+    const int row = chunk / CPR, pos = chunk % CPR;
+    drow[i] = row;
+    offK[i] = (uint32_t)(row * D * 2 + (pos ^ swz_dual<D>(row)) * 16);
+    offV[i] = (uint32_t)(row * D * 2 + (pos ^ swz_rowread<D>(row)) * 16);
+  }
+  const uint32_t head_bytes = BIG ? 0u : (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(Kh, head_bytes);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(Vh, head_bytes);
+  auto issue = [&](int j) {
+    uint8_t* st = smem + (j & 1) * Cfg::STAGE_B + w * 64 * 16;
+    if (!BIG && (j + 1) * BK <= N) {
+      const uint32_t soff = (uint32_t)(j * BK) * (D * 2);
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        buffer_lds16(rK, st + i * NT * 16, offK[i], soff);
+        buffer_lds16(rV, st + TILE_B + i * NT * 16, offV[i], soff);
       }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* Ks = smem + buf * Cfg::STAGE;
-    uint16_t* Vs = Ks + Cfg::KBUF;
+    } else {
+      // ragged last tile (or a huge head): rows past the end repeat row N - 1 (masked below)
 #pragma unroll
-    for (int i = 0; i < Cfg::CH; ++i) {
-      const int c = tid + i * Cfg::NT;
-      const int row = c / Cfg::CPR;
-      const int col = c % Cfg::CPR;
-      *(u32x4*)(Ks + row * Cfg::KSTR + col * 8) = kr[i];
-      *(u32x4*)(Vs + row * Cfg::VSTR + col * 8) = vr[i];
+      for (int i = 0; i < LPT; ++i) {
+        const size_t src_row = (size_t)min(j * BK + drow[i], N - 1) * (D * 2);
+        const uint32_t in_row = (uint32_t)(drow[i] * D * 2);
+        global_lds16((const uint8_t*)Kh + src_row + (offK[i] - in_row), st + i * NT * 16);
+        global_lds16((const uint8_t*)Vh + src_row + (offV[i] - in_row), st + TILE_B + i * NT * 16);
+      }
     }
   };
 
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  load_tile(0);
-  store_tile(0);
+  issue(0);
   for (int j = 0; j < n_kv; ++j) {
-    if (j + 1 < n_kv) load_tile(j + 1);
-    __syncthreads();
+    wait_vmcnt<0>();
+    barrier_lds();
+    if (j + 1 < n_kv) issue(j + 1);
     const int k0 = j * BK;
-    if (wave_active && k0 < wave_kv_end) {
-      const uint16_t* Ks = smem + (j & 1) * Cfg::STAGE;
-      const uint16_t* Vs = Ks + Cfg::KBUF;
-      const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > q0);
-      vec8 dsp[BK / 16];
+    if (!(wave_active && k0 < wave_kv_end)) continue;
+    const uint8_t* Ks = smem + (j & 1) * Cfg::STAGE_B;
+    const uint8_t* Vs = Ks + TILE_B;
+    const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > q0);
+    vec8 dsp[BK / 16];
 #pragma unroll
-      for (int kb = 0; kb < BK / 32; ++kb) {
-        f32x16 s, dp;
+    for (int kb = 0; kb < BK / 32; ++kb) {
+      f32x16 s, dp;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          s[e] = 0.f;
-          dp[e] = 0.f;
-        }
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {  // two independent chains, interleaved
-          const vec8 ka = *(const vec8*)(Ks + (kb * 32 + lr) * Cfg::KSTR + 16 * st + 8 * h);
-          const vec8 va = *(const vec8*)(Vs + (kb * 32 + lr) * Cfg::VSTR + 16 * st + 8 * h);
-          s = TR::mma(ka, qf[st], s);
-          dp = TR::mma(va, df[st], dp);
-        }
-        // element e is key k0 + kb*32 + 8(e>>2) + 4h + (e&3), query qrow
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          u32x4 packed;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            float ds2[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int e = 8 * half + 2 * e2 + u;
-              float pv = __builtin_amdgcn_exp2f(fmaf(s[e], a.c, -lse2));
-              if (need_mask) {
-                const int kk = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-                pv = (kk >= N || (CAUSAL && kk > qrow)) ? 0.f : pv;
-              }
-              ds2[u] = pv * (dp[e] - dval);
-            }
-            packed[e2] = TR::pack2(ds2[0], ds2[1]);
-          }
-          dsp[2 * kb + half] = bitcast<vec8>(packed);
-        }
+      for (int e = 0; e < 16; ++e) {
+        s[e] = 0.f;
+        dp[e] = 0.f;
       }
-      // dQ^T += K^T dS^T
+      const int row = kb * 32 + lr;
 #pragma unroll
-      for (int c = 0; c < BK / 16; ++c) {
+      for (int st = 0; st < D / 16; ++st) {  // two independent chains, interleaved
+        const vec8 ka = *(const vec8*)(Ks + row_read_addr<D>(row, 2 * st + h));
+        const vec8 va = *(const vec8*)(Vs + row * (D * 2) + (((2 * st + h) ^ swz_rowread<D>(row)) << 4));
+        s = TR::mma(ka, qf[st], s);
+        dp = TR::mma(va, df[st], dp);
+      }
+      // element e is key k0 + kb*32 + 8(e>>2) + 4h + (e&3), query qrow
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b) {
-          const uint16_t* p0 = Ks + (16 * c + tr_row) * Cfg::KSTR + 32 * b + tr_col;
-          const i16x4 lo = lds_read_tr16(p0);
-          const i16x4 hi = lds_read_tr16(p0 + 8 * Cfg::KSTR);
-          const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[b] = TR::mma(bitcast<vec8>(both), dsp[c], acc[b]);
+      for (int half = 0; half < 2; ++half) {
+        u32x4 packed;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          float ds2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int e = 8 * half + 2 * e2 + u;
+            float pv = __builtin_amdgcn_exp2f(fmaf(s[e], a.c, -lse2));
+            if (need_mask) {
+              const int kk = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+              pv = (kk >= N || (CAUSAL && kk > qrow)) ? 0.f : pv;
+            }
+            ds2[u] = pv * (dp[e] - dval);
+          }
+          packed[e2] = TR::pack2(ds2[0], ds2[1]);
         }
+        dsp[2 * kb + half] = bitcast<vec8>(packed);
       }
     }
-    if (j + 1 < n_kv) store_tile((j + 1) & 1);
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int c = 0; c < BK / 16; ++c) {
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b) {
+        const i16x4 lo = lds_read_tr16(Ks + tr_read_addr<D>(16 * c + tr_row, 32 * b + tr_col));
+        const i16x4 hi = lds_read_tr16(Ks + tr_read_addr<D>(16 * c + tr_row + 8, 32 * b + tr_col));
+        const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[b] = TR::mma(bitcast<vec8>(both), dsp[c], acc[b]);
+      }
+    }
   }
 
   if (!wave_active || qrow >= N) return;
@@ -497,23 +582,33 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stage < 0 || stage == 1) {
+  const bool big = (size_t)r.N * D * 2 >= ((size_t)1 << 31);
+  a.bh_total = (int)BH;
+  if (stage < 0 || stage == 1 || stage == 3 || stage == 4) {
     a.ntiles = (r.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
     dim3 g1((unsigned)(BH * a.ntiles));
-    if (r.causal)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<TR, D, true>), g1, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<TR, D, false>), g1, dim3(256), 0, st, a);
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, g1, dim3(256), 0, st, a); };
+    const bool dv_pass = stage != 4, dk_pass = stage != 3;
+    if (r.causal) {
+      if (dv_pass) big ? go(bwd_dkdv_kernel<TR, D, true, true, 1>) : go(bwd_dkdv_kernel<TR, D, true, false, 1>);
+      if (dk_pass) big ? go(bwd_dkdv_kernel<TR, D, true, true, 2>) : go(bwd_dkdv_kernel<TR, D, true, false, 2>);
+    } else {
+      if (dv_pass) big ? go(bwd_dkdv_kernel<TR, D, false, true, 1>) : go(bwd_dkdv_kernel<TR, D, false, false, 1>);
+      if (dk_pass) big ? go(bwd_dkdv_kernel<TR, D, false, true, 2>) : go(bwd_dkdv_kernel<TR, D, false, false, 2>);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stage < 0 || stage == 2) {
     a.ntiles = (r.N + DqCfg<D>::BQ - 1) / DqCfg<D>::BQ;
     dim3 g2((unsigned)(BH * a.ntiles));
-    if (r.causal)
-      hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true>), g2, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false>), g2, dim3(256), 0, st, a);
+    if (r.causal) {
+      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, true>), g2, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, false>), g2, dim3(256), 0, st, a);
+    } else {
+      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, true>), g2, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, false>), g2, dim3(256), 0, st, a);
+    }
     e = hipGetLastError();
   }
   return e;

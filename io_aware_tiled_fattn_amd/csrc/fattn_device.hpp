@@ -126,6 +126,14 @@ template <int D>
 __device__ inline int swz_rowread(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
 template <int D>
 __device__ inline int swz_trread(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+// For tiles read both ways (row reads of 16 consecutive rows at one chunk, and transposed reads
+// of 4-row x 4-chunk blocks): the low row bits pick the 4-chunk group, the next bits the chunk
+// inside it, so both patterns touch distinct 16-byte bank slots. Individual chunks move, so a
+// transposed read addresses each lane's chunk separately (tr_read_addr).
+template <int D>
+__device__ inline int swz_dual(int row) {
+  return D == 128 ? 4 * (row & 3) + ((row >> 2) & 3) : 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+}
 
 // Block index remap so that consecutive logical blocks share an XCD: hardware dispatches block
 // ids round-robin over the 8 XCDs, so physical id x runs on XCD x % 8. When the grid is a

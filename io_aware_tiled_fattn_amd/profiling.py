@@ -27,11 +27,13 @@ COPY_BYTES = 256 * 2**20  # the calibration copy reads and writes this many byte
 
 COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {run}/trace -o run -- "
-             "python -u bench.py --steps 10 --warmup 3 --no-cpu-baseline",
+             "python -u bench.py --steps 10 --warmup 3 --no-cpu-baseline --clock-warmup-s 0.5",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {run}/fetch -o run -- "
-             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy",
+             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy "
+             "--clock-warmup-s 0",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {run}/write -o run -- "
-             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy",
+             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy "
+             "--clock-warmup-s 0",
 }
 
 
