@@ -82,6 +82,7 @@ __device__ inline i16x4 lds_read_tr16(const void* p) {
 
 __device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+
 // ---- direct global -> LDS loads (buffer_load_dwordx4 ... lds) --------------------------------
 // One instruction moves 16 bytes per lane from memory straight into LDS, without VGRPs: lane i's
 // 16 bytes land at LDS byte (lds + 16 * i), where lds is the same for the whole wave. The source

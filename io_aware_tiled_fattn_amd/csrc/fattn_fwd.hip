@@ -183,18 +183,11 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_colb = (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;  // byte offset in a 64-B group
 
-  issue(0);
-  for (int j = 0; j < n_kv; ++j) {
-    wait_vmcnt<0>();  // this wave's loads of tile j have landed
-    barrier_lds();    // ... and everyone's; stage (j + 1) & 1 is no longer being read
-    if (j + 1 < n_kv) issue(j + 1);
+  // S^T = K Q^T for tile j (BC/32 independent 32-key accumulator chains), masked on diagonal and
+  // ragged tiles; returns the row max of the log2-domain logits.
+  auto scores = [&](int j, f32x16 (&s)[BC / 32]) {
     const int k0 = j * BC;
-    if (!(wave_active && k0 < wave_kv_end)) continue;
     const uint8_t* Ks = smem + (j & 1) * Cfg::STAGE_B;
-    const uint8_t* Vs = Ks + TILE_B;
-
-    // S^T = K Q^T for BC/32 blocks of 32 keys; the BC/32 accumulators are independent chains.
-    f32x16 s[BC / 32];
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
@@ -216,7 +209,6 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * (BC / 32), 0);
 
-    // Mask (diagonal and ragged tiles only), then the row max of the raw scores.
     const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
     if (need_mask) {
       // element (kb, e) holds key k0 + kb*32 + 8(e>>2) + 4h + (e&3); it is masked when that
@@ -235,23 +227,13 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    mx = max_halves(mx) * a.c;  // c > 0, so this is the max of the log2-domain logits
-
-    // Move the reference max only when it grew by more than the slack.
-    const float m_new = fmaxf(m_ref, mx);
-    const bool grow = m_new > m_ref + kRescaleSlack;
-    if (wave_any(grow)) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
-      if (grow) m_ref = m_new;
-      l_part *= alpha;
-#pragma unroll
-      for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
-    }
-
-    // P^T = exp2(s*c - m_ref) (masked scores are -inf and give 0), packed to 16-bit MFMA B
-    // fragments (8 keys per 16-key chunk).
+    return max_halves(mx) * a.c;  // c > 0, so this is the max of the log2-domain logits
+  };
+  // P^T = exp2(s*c - m_ref) (masked scores are -inf and give 0), packed to 16-bit MFMA B
+  // fragments (8 keys per 16-key chunk), then O^T += V^T P^T with V^T fragments from the
+  // transposed LDS read (rows 16c + tr_row and +8).
+  auto softmax_pv = [&](int j, const f32x16 (&s)[BC / 32]) {
+    const uint8_t* Vs = smem + (j & 1) * Cfg::STAGE_B + TILE_B;
     const float neg_m = -m_ref;
     vec8 pf[BC / 16];
     float ls = 0.f;
@@ -270,8 +252,6 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
         pf[2 * kb + half] = bitcast<vec8>(packed);
       }
     l_part += ls;
-
-    // O^T += V^T P^T; V^T fragments via the transposed LDS read (rows 16c + tr_row and +8).
 #pragma unroll
     for (int c = 0; c < BC / 16; ++c) {
 #pragma unroll
@@ -285,6 +265,43 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
         acc[b] = TR::mma(bitcast<vec8>(both), pf[c], acc[b]);
       }
     }
+  };
+
+  // The tile loop leaves as soon as some row's max outgrows the slack; the rescale (rare) is
+  // done outside it and the loop resumes. Keeping the conditional rescale out of the loop body
+  // keeps the accumulator in one set of registers (a join inside the loop made the compiler copy
+  // all of it on every tile).
+  issue(0);
+  int j = 0;
+  f32x16 s[BC / 32];
+  float m_new = 0.f;
+  while (j < n_kv) {
+    bool grew = false;
+    for (; j < n_kv; ++j) {
+      wait_vmcnt<0>();  // this wave's loads of tile j have landed
+      barrier_lds();    // ... and everyone's; stage (j + 1) & 1 is no longer being read
+      if (j + 1 < n_kv) issue(j + 1);
+      if (!(wave_active && j * BC < wave_kv_end)) continue;
+      const float mx = scores(j, s);
+      m_new = fmaxf(m_ref, mx);
+      if (wave_any(m_new > m_ref + kRescaleSlack)) {
+        grew = true;
+        break;
+      }
+      softmax_pv(j, s);
+    }
+    if (!grew) break;
+    // Move the reference max of the rows that outgrew it, rescale their state, finish tile j.
+    const bool grow = m_new > m_ref + kRescaleSlack;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+    if (grow) m_ref = m_new;
+    l_part *= alpha;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
+    softmax_pv(j, s);
+    ++j;
   }
 
   if (!wave_active) return;
