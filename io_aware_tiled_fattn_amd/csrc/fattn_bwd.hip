@@ -204,12 +204,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   // Load i of this thread fills LDS chunk i*NT + tid of a Q (dO) tile with the source chunk
   // (chunk % CPR) ^ swz_dual(row) of row chunk / CPR.
   uint32_t off[LPT];
-  int drow[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int chunk = i * NT + tid;
     const int row = chunk / CPR, pos = chunk % CPR;
-    drow[i] = row;
     off[i] = (uint32_t)(row * D * 2 + (pos ^ swz_dual<D>(row)) * 16);
   }
   const uint32_t head_bytes = BIG ? 0u : (uint32_t)N * D * 2;
@@ -229,8 +227,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       // are zeroed below, so they add nothing
 #pragma unroll
       for (int t = 0; t < LPT; ++t) {
-        const size_t src_row = (size_t)min(i * BQ + drow[t], N - 1) * (D * 2);
-        const uint32_t in_row = off[t] - (uint32_t)(drow[t] * D * 2);
+        const size_t src_row = (size_t)min(i * BQ + (t * NT + tid) / CPR, N - 1) * (D * 2);
+        const uint32_t in_row = off[t] - (uint32_t)((t * NT + tid) / CPR * D * 2);
         global_lds16((const uint8_t*)Qh + src_row + in_row, st + t * NT * 16);
         global_lds16((const uint8_t*)dOh + src_row + in_row, st + TILE_B + t * NT * 16);
       }
@@ -289,26 +287,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         for (int st = 0; st < D / 16; ++st) {  // two independent chains, interleaved
           const int addr = row_read_addr<D>(qb * 32 + lr, 2 * st + h);
           const vec8 qa = *(const vec8*)(Qs + addr);
-          const vec8 da = *(const vec8*)(dOs + addr);
           s = TR::mma(qa, kf[st], s);
-          if (DO_DK) dp = TR::mma(da, vf[st], dp);
+          if (DO_DK) {
+            const vec8 da = *(const vec8*)(dOs + addr);
+            dp = TR::mma(da, vf[st], dp);
+          }
         }
-        // element 4j + r is query qb*32 + 8j + 4h + r of the tile, key = this lane's key
-        float p[16], ds[16];
+        // keep the fragment reads one step ahead of the MFMAs that consume them
+        constexpr int PER = DO_DK ? 2 : 1;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PER, 0);
+#pragma unroll
+        for (int st = 0; st < D / 16 - 2; ++st) {
+          __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * PER, 0);
+        // element 4j + r is query qb*32 + 8j + 4h + r of the tile, key = this lane's key; the
+        // exponent (in place in s) is the log2-domain logit minus the row's log2 LSE, -inf
+        // where masked (P = 0 there)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const f32x4 l4 = *(const f32x4*)(lse2s + qb * 32 + 8 * j + 4 * h);
-          const f32x4 d4 = *(const f32x4*)(dvs + qb * 32 + 8 * j + 4 * h);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[4 * j + r] = fmaf(s[4 * j + r], a.c, -l4[r]);
+        }
+        if (need_mask) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int qq = q_base + qb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+            s[e] = ((CAUSAL && key > qq) || qq >= N) ? -__builtin_inff() : s[e];
+          }
+        }
+        float p[16], ds[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+          if (DO_DK) d4 = *(const f32x4*)(dvs + qb * 32 + 8 * j + 4 * h);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int e = 4 * j + r;
-            float pv = __builtin_amdgcn_exp2f(fmaf(s[e], a.c, -l4[r]));
-            if (need_mask) {
-              const int qq = q_base + qb * 32 + 8 * j + 4 * h + r;
-              pv = ((CAUSAL && key > qq) || qq >= N) ? 0.f : pv;
-            }
-            p[e] = pv;
-            ds[e] = pv * (dp[e] - d4[r]);
+            p[e] = __builtin_amdgcn_exp2f(s[e]);
+            ds[e] = p[e] * (dp[e] - d4[r]);
           }
         }
         vec8 pp[2], dsp[2];
@@ -442,12 +461,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 
   // K tiles are read both row-wise and transposed (swz_dual); V tiles only row-wise.
   uint32_t offK[LPT], offV[LPT];
-  int drow[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int chunk = i * NT + tid;
     const int row = chunk / CPR, pos = chunk % CPR;
-    drow[i] = row;
     offK[i] = (uint32_t)(row * D * 2 + (pos ^ swz_dual<D>(row)) * 16);
     offV[i] = (uint32_t)(row * D * 2 + (pos ^ swz_rowread<D>(row)) * 16);
   }
@@ -467,8 +484,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       // ragged last tile (or a huge head): rows past the end repeat row N - 1 (masked below)
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
-        const size_t src_row = (size_t)min(j * BK + drow[i], N - 1) * (D * 2);
-        const uint32_t in_row = (uint32_t)(drow[i] * D * 2);
+        const size_t src_row = (size_t)min(j * BK + (i * NT + tid) / CPR, N - 1) * (D * 2);
+        const uint32_t in_row = (uint32_t)((i * NT + tid) / CPR * D * 2);
         global_lds16((const uint8_t*)Kh + src_row + (offK[i] - in_row), st + i * NT * 16);
         global_lds16((const uint8_t*)Vh + src_row + (offV[i] - in_row), st + TILE_B + i * NT * 16);
       }
@@ -488,7 +505,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     const uint8_t* Ks = smem + (j & 1) * Cfg::STAGE_B;
     const uint8_t* Vs = Ks + TILE_B;
     const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > q0);
-    vec8 dsp[BK / 16];
 #pragma unroll
     for (int kb = 0; kb < BK / 32; ++kb) {
       f32x16 s, dp;
@@ -505,37 +521,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         s = TR::mma(ka, qf[st], s);
         dp = TR::mma(va, df[st], dp);
       }
-      // element e is key k0 + kb*32 + 8(e>>2) + 4h + (e&3), query qrow
+      // element e is key k0 + kb*32 + 8(e>>2) + 4h + (e&3), query qrow; the exponent (in place
+      // in s) is the log2-domain logit minus the row's log2 LSE, -inf where masked (P = 0 there)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = fmaf(s[e], a.c, -lse2);
+      if (need_mask) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kk = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+          s[e] = (kk >= N || (CAUSAL && kk > qrow)) ? -__builtin_inff() : s[e];
+        }
+      }
+      vec8 dsp[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         u32x4 packed;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          float ds2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int e = 8 * half + 2 * e2 + u;
-            float pv = __builtin_amdgcn_exp2f(fmaf(s[e], a.c, -lse2));
-            if (need_mask) {
-              const int kk = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-              pv = (kk >= N || (CAUSAL && kk > qrow)) ? 0.f : pv;
-            }
-            ds2[u] = pv * (dp[e] - dval);
-          }
-          packed[e2] = TR::pack2(ds2[0], ds2[1]);
+          const int e = 8 * half + 2 * e2;
+          const float ds0 = __builtin_amdgcn_exp2f(s[e]) * (dp[e] - dval);
+          const float ds1 = __builtin_amdgcn_exp2f(s[e + 1]) * (dp[e + 1] - dval);
+          packed[e2] = TR::pack2(ds0, ds1);
         }
-        dsp[2 * kb + half] = bitcast<vec8>(packed);
+        dsp[half] = bitcast<vec8>(packed);
       }
-    }
-    // dQ^T += K^T dS^T
+      // dQ^T += K^T dS^T over this block's two 16-key chunks
 #pragma unroll
-    for (int c = 0; c < BK / 16; ++c) {
+      for (int half = 0; half < 2; ++half) {
+        const int c = 2 * kb + half;
 #pragma unroll
-      for (int b = 0; b < D / 32; ++b) {
-        const i16x4 lo = lds_read_tr16(Ks + tr_read_addr<D>(16 * c + tr_row, 32 * b + tr_col));
-        const i16x4 hi = lds_read_tr16(Ks + tr_read_addr<D>(16 * c + tr_row + 8, 32 * b + tr_col));
-        const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[b] = TR::mma(bitcast<vec8>(both), dsp[c], acc[b]);
+        for (int b = 0; b < D / 32; ++b) {
+          const i16x4 lo = lds_read_tr16(Ks + tr_read_addr<D>(16 * c + tr_row, 32 * b + tr_col));
+          const i16x4 hi = lds_read_tr16(Ks + tr_read_addr<D>(16 * c + tr_row + 8, 32 * b + tr_col));
+          const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[b] = TR::mma(bitcast<vec8>(both), dsp[half], acc[b]);
+        }
       }
     }
   }

@@ -138,12 +138,10 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   // Load i of this thread fills LDS chunk i*NT + tid of a tile: row r = chunk / CPR holds, at
   // chunk position p = chunk % CPR, the source chunk p ^ swizzle(r).
   uint32_t offK[LPT], offV[LPT];  // byte offsets within a tile: row * 2D + source chunk * 16
-  int drow[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int chunk = i * NT + tid;
     const int row = chunk / CPR, pos = chunk % CPR;
-    drow[i] = row;
     offK[i] = (uint32_t)(row * D * 2 + (pos ^ swz_rowread<D>(row)) * 16);
     offV[i] = (uint32_t)(row * D * 2 + (pos ^ swz_trread<D>(row)) * 16);
   }
@@ -164,8 +162,8 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
       // holds real, finite data; those keys are masked below
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
-        const size_t src_row = (size_t)min(j * BC + drow[i], N - 1) * (D * 2);
-        const uint32_t in_row = (uint32_t)(drow[i] * D * 2);
+        const size_t src_row = (size_t)min(j * BC + (i * NT + tid) / CPR, N - 1) * (D * 2);
+        const uint32_t in_row = (uint32_t)((i * NT + tid) / CPR * D * 2);
         global_lds16((const uint8_t*)Kh + src_row + (offK[i] - in_row), st + i * NT * 16);
         global_lds16((const uint8_t*)Vh + src_row + (offV[i] - in_row), st + TILE_B + i * NT * 16);
       }
