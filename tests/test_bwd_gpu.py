@@ -137,3 +137,26 @@ def test_backward_causal_prefix_invariance():
     o2, lse2 = fa.forward(q, k2, v2, causal=True)
     dq2, _, _ = fa.backward(q, k2, v2, o2, do, lse2, causal=True)
     assert torch.equal(dq1[:, :, : cut + 1], dq2[:, :, : cut + 1])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [100, 300])
+def test_backward_stage_entry_points_match_fattn_bwd(causal, N):
+    """preprocess, dK/dV (= dV pass then dK pass) and dQ called one by one give fattn_bwd's
+    results bit for bit; the dV and dK passes alone give the dkdv stage's dV and dK."""
+    import torch
+    fa = _fa()
+    inp = fi.make_inputs((1, 3, N, 128), "bf16", 31 + N, with_do=True)
+    q, k, v, do = upload(inp)
+    o, lse = fa.forward(q, k, v, causal=causal)
+    ref = fa.backward(q, k, v, o, do, lse, causal=causal)
+    dvec = torch.empty(1 * 3 * N, dtype=torch.float32, device="cuda")
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    fa.backward_stages(q, k, v, o, do, lse, dq, dk, dv, dvec, causal=causal, stages=(0, 1, 2))
+    torch.cuda.synchronize()
+    for x, y in zip((dq, dk, dv), ref):
+        assert torch.equal(x, y)
+    dk2, dv2 = torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
+    fa.backward_stages(q, k, v, o, do, lse, dq, dk2, dv2, dvec, causal=causal, stages=(3, 4))
+    torch.cuda.synchronize()
+    assert torch.equal(dk2, ref[1]) and torch.equal(dv2, ref[2])
