@@ -56,6 +56,32 @@ WORKLOADS = {
     5: Workload(5, "training bf16 forward+backward", "bf16", 2, 16, 4096, 128, ("causal",), True),
 }
 
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """A decode-shaped workload: Nq new query rows per head against an Nk-long key/value cache."""
+
+    ident: int
+    name: str
+    dtype: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# Split-KV forward workloads: one query per head (token-by-token decode) and 16 (a block of
+# draft tokens checked at once), both over a 16384-key cache at d = 128.
+DECODE_WORKLOADS = {
+    6: DecodeWorkload(6, "decode bf16 split-KV forward", "bf16", 8, 32, 1, 16384, 128),
+    7: DecodeWorkload(7, "multi-token decode bf16 split-KV forward", "bf16", 8, 32, 16, 16384, 128),
+}
+
 # Variants: 0 = base draw; 1 = every logit shifted by exactly +500 (Q[...,0] = 1 and
 # K[...,0] += 500/scale, see ``shifted_pair``); 2 = the literal construction where only K[...,0]
 # gets the +500/scale offset, so row i moves by 500*q[i,0].
@@ -132,6 +158,14 @@ def make_inputs(shape, dtype: str, seed: int, variant: int = VARIANT_BASE, with_
     if with_do:
         bits["do"] = dob
     return Inputs(dtype, q, k, v, do, bits)
+
+
+def make_decode_inputs(B, H, nq, nk, d, dtype: str, seed: int, variant: int = VARIANT_BASE) -> Inputs:
+    """Seeded Q [B, H, nq, d] and K, V [B, H, nk, d], rounded to ``dtype`` (no dO)."""
+    q, qb = draw((B, H, nq, d), (seed, variant, _Q), dtype)
+    k, kb = draw((B, H, nk, d), (seed, variant, _K), dtype)
+    v, vb = draw((B, H, nk, d), (seed, variant, _V), dtype)
+    return Inputs(dtype, q, k, v, None, {"q": qb, "k": kb, "v": vb})
 
 
 def unshifted_partner(inp: Inputs, scale: float) -> Inputs:

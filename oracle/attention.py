@@ -6,7 +6,7 @@ Forward (page "FlashAttention为什么更快更省显存", opening formula; page
 section on why softmax needs a whole row, and its stable reference ``naive_attention`` that
 subtracts the row max before the exponential):
 
-    S = scale * Q K^T,  S[i, j] = -inf where causal and j > i
+    S = scale * Q K^T,  S[i, j] = -inf where causal and j > i + causal_offset
     m_i = max_j S[i, j],  P[i, j] = exp(S[i, j] - m_i),  l_i = sum_j P[i, j]
     O_i = (sum_j P[i, j] V_j) / l_i,  LSE_i = m_i + ln l_i
 
@@ -24,6 +24,12 @@ rule, for a loss L with dO = dL/dO:
 
 Everything is computed in float64 over whole rows of S, a chunk of rows at a time so that the
 N = 16384 workload fits in host memory. No online merge happens here.
+
+Queries and keys of different lengths (decode against a key/value cache, page "mianstack
+q-0277", backward section, which names the cache): the pages fix no causal convention for that
+case. The reading taken here is that the Nq queries are the LAST Nq positions of the Nk-long
+sequence, so query i sits at position i + (Nk - Nq) and sees keys j <= i + causal_offset with
+causal_offset = Nk - Nq. With Nq == Nk the offset is 0 and this is the ordinary causal mask.
 """
 from __future__ import annotations
 
@@ -46,11 +52,12 @@ def _masked_scores(q_rows, k, scale, causal, row0):
     return s
 
 
-def forward_slice(q, k, v, scale, causal=False, rows=None, chunk=_CHUNK):
-    """O and LSE for one (b, h) slice. q: [Nq, d], k, v: [N, d]; float64 results.
+def forward_slice(q, k, v, scale, causal=False, rows=None, chunk=_CHUNK, causal_offset=0):
+    """O and LSE for one (b, h) slice. q: [Nq, d], k, v: [Nk, d]; float64 results.
 
-    ``rows`` optionally restricts the computation to those query indices (then q holds all N
-    rows and only the selected ones are evaluated, in the order given).
+    ``rows`` optionally restricts the computation to those query indices (then q holds all
+    rows and only the selected ones are evaluated, in the order given). With ``causal``, query i
+    sees keys j <= i + causal_offset; every evaluated row must see at least one key.
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     idx = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -60,7 +67,7 @@ def forward_slice(q, k, v, scale, causal=False, rows=None, chunk=_CHUNK):
         sel = idx[c0:c0 + chunk]
         s = (q[sel] @ k.T) * scale
         if causal:
-            s[np.arange(k.shape[0])[None, :] > sel[:, None]] = -np.inf
+            s[np.arange(k.shape[0])[None, :] > sel[:, None] + causal_offset] = -np.inf
         m = s.max(axis=1)
         p = np.exp(s - m[:, None])
         l = p.sum(axis=1)
@@ -69,8 +76,8 @@ def forward_slice(q, k, v, scale, causal=False, rows=None, chunk=_CHUNK):
     return out, lse
 
 
-def forward(q, k, v, scale, causal=False, rows=None, heads=None):
-    """O [B,H,n,d] and LSE [B,H,n] for inputs [B,H,N,d].
+def forward(q, k, v, scale, causal=False, rows=None, heads=None, causal_offset=0):
+    """O [B,H,n,d] and LSE [B,H,n] for q [B,H,Nq,d] and k, v [B,H,Nk,d].
 
     ``heads`` optionally lists (b, h) pairs to evaluate (others are left NaN); ``rows`` limits
     every evaluated head to those query rows (n = len(rows)).
@@ -82,7 +89,8 @@ def forward(q, k, v, scale, causal=False, rows=None, heads=None):
     lse = np.full((B, H, n), np.nan)
     pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
     for b, h in pairs:
-        o[b, h], lse[b, h] = forward_slice(q[b, h], k[b, h], v[b, h], scale, causal, rows)
+        o[b, h], lse[b, h] = forward_slice(q[b, h], k[b, h], v[b, h], scale, causal, rows,
+                                           causal_offset=causal_offset)
     return o, lse
 
 
