@@ -31,7 +31,8 @@
  *    partial overlap is undefined behaviour).
  *  - Supported: d in {64, 128}; 1 <= N <= 16777216; B, H >= 1 with B*H*N*d < 2^46; `scale`
  *    finite (0 gives uniform attention, negative values are allowed); causal in {0, 1}.
- *    Causal masks key j > query i (queries and keys share the same length N).
+ *    Causal masks key j > query i (queries and keys share the same length N), except in the
+ *    split-KV entry points below, where Nq and Nk may differ.
  */
 #ifndef FATTN_H
 #define FATTN_H
@@ -127,6 +128,61 @@ int fattn_bwd_dk(const void* q, const void* k, const void* v, const void* dO, co
 int fattn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                  const float* dvec, void* dq, int B, int H, int N, int d, float scale, int causal,
                  int dtype, void* stream);
+
+/*
+ * Split-KV forward: Nq query rows per head against an Nk-long key/value cache, computed as
+ * per-range partial results merged afterwards. This is the decode shape (page "mianstack q-0277",
+ * backward section, names the key/value cache): the keys of each row are cut into num_splits
+ * ranges so that many work-groups stream K/V at once, then the partials are merged with the
+ * two-state rule of page 3's section on keeping the blockwise softmax normalised (max, rescaled
+ * exp-sums, rescaled outputs).
+ *
+ * Layout: q [B,H,Nq,d]; k, v [B,H,Nk,d] (dtype FATTN_F16 or FATTN_BF16); o [B,H,Nq,d] (dtype);
+ * lse [B,H,Nq] (float32). Partials: o_parts [S,B,H,Nq,d] and lse_parts [S,B,H,Nq], float32, S =
+ * num_splits. Limits: 1 <= Nq, Nk <= 16777216; 1 <= num_splits <= 1024; d in {64, 128}.
+ *
+ * Partition: split s covers keys [s*L, min(Nk, (s+1)*L)) with L = 64 * ceil(Nk / (64 * S)); splits
+ * starting at or after Nk are empty.
+ * Causal: query i is position i + Nk - Nq of the sequence and sees keys j <= i + Nk - Nq (the
+ * queries are the last Nq positions; Nq == Nk is the ordinary causal mask). causal with Nq > Nk
+ * returns FATTN_ERR_SHAPE.
+ * Partial of split s for row i: O_s = softmax-weighted mean of the split's visible values and
+ * LSE_s = natural log of the exp-sum of the split's visible scaled logits; a row that sees no key
+ * of the split gets O_s = 0, LSE_s = -inf.
+ */
+
+/* num_splits that fattn_fwd_splitkv picks when given 0 (0 if the shape is invalid). */
+int fattn_splitkv_num_splits(int B, int H, int Nq, int Nk, int d);
+
+/*
+ * Bytes of workspace fattn_fwd_splitkv needs for num_splits (0 = the automatic choice): the
+ * float32 partials, o_parts then lse_parts, each rounded up to 256 bytes. 0 for invalid shapes.
+ */
+size_t fattn_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits);
+
+/*
+ * O and LSE by fattn_fwd_partial into the workspace followed by fattn_combine, both enqueued on
+ * `stream`. num_splits = 0 picks fattn_splitkv_num_splits(). The workspace is caller-owned device
+ * memory of at least fattn_fwd_splitkv_workspace_size() bytes; contents on exit unspecified.
+ */
+int fattn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                      int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The partials alone (num_splits >= 1): writes o_parts and lse_parts as described above. */
+int fattn_fwd_partial(const void* q, const void* k, const void* v, float* o_parts, float* lse_parts,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                      int num_splits, void* stream);
+
+/*
+ * Merge of S = num_splits float32 partials per row into o [B,H,Nq,d] (dtype: FATTN_F32, FATTN_F16
+ * or FATTN_BF16, round-to-nearest-even) and lse [B,H,Nq] (float32). With M = max_s LSE_s and
+ * w_s = exp(LSE_s - M): O = sum_s w_s O_s / sum_s w_s and LSE = M + ln sum_s w_s; partials with
+ * LSE_s = -inf are skipped (their O_s is not read), and a row whose partials are all -inf gets
+ * O = 0, LSE = -inf. Any partials in this layout can be merged, not only fattn_fwd_partial's.
+ */
+int fattn_combine(const float* o_parts, const float* lse_parts, int num_splits, void* o, float* lse,
+                  int B, int H, int Nq, int d, int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fattn_strerror(int status);

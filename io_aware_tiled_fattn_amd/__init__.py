@@ -6,9 +6,11 @@ stream; there is no CPU or PyTorch fallback, and a missing library raises.
 
 Low-level names mirror the C entry points (``fattn_fwd``, ``fattn_fwd_tiled``, ``fattn_bwd``,
 ``fattn_bwd_workspace_size``, ``fattn_bwd_preprocess``, ``fattn_bwd_dkdv``, ``fattn_bwd_dv``,
-``fattn_bwd_dk``, ``fattn_bwd_dq``,
-``fattn_strerror``, ``fattn_version``) and take raw device addresses. ``forward``, ``backward``
-and ``backward_stages`` wrap them for contiguous [B, H, N, d] torch tensors.
+``fattn_bwd_dk``, ``fattn_bwd_dq``, ``fattn_fwd_splitkv``, ``fattn_fwd_splitkv_workspace_size``,
+``fattn_splitkv_num_splits``, ``fattn_fwd_partial``, ``fattn_combine``,
+``fattn_strerror``, ``fattn_version``) and take raw device addresses. ``forward``, ``backward``,
+``backward_stages``, ``forward_splitkv``, ``forward_partial`` and ``combine`` wrap them for
+contiguous torch tensors.
 """
 from __future__ import annotations
 
@@ -21,6 +23,8 @@ __all__ = [
     "fattn_fwd", "fattn_fwd_tiled", "fattn_bwd", "fattn_bwd_workspace_size", "fattn_strerror",
     "fattn_bwd_preprocess", "fattn_bwd_dkdv", "fattn_bwd_dv", "fattn_bwd_dk", "fattn_bwd_dq",
     "fattn_version", "forward", "backward", "backward_stages", "dtype_code",
+    "fattn_fwd_splitkv", "fattn_fwd_splitkv_workspace_size", "fattn_splitkv_num_splits",
+    "fattn_fwd_partial", "fattn_combine", "forward_splitkv", "forward_partial", "combine",
 ]
 
 FATTN_F32, FATTN_F16, FATTN_BF16 = 0, 1, 2
@@ -65,6 +69,16 @@ def lib():
     for name in ("fattn_bwd_dv", "fattn_bwd_dk", "fattn_bwd_dq"):
         getattr(L, name).argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
         getattr(L, name).restype = i
+    L.fattn_splitkv_num_splits.argtypes = [i, i, i, i, i]
+    L.fattn_splitkv_num_splits.restype = i
+    L.fattn_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i, i]
+    L.fattn_fwd_splitkv_workspace_size.restype = sz
+    L.fattn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    L.fattn_fwd_splitkv.restype = i
+    L.fattn_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    L.fattn_fwd_partial.restype = i
+    L.fattn_combine.argtypes = [vp, vp, i, vp, vp, i, i, i, i, i, vp]
+    L.fattn_combine.restype = i
     L.fattn_strerror.argtypes = [i]
     L.fattn_strerror.restype = ctypes.c_char_p
     L.fattn_version.argtypes = []
@@ -112,6 +126,30 @@ def fattn_bwd_dk(q, k, v, dO, lse, dvec, dk, B, H, N, d, scale, causal, dtype, s
 
 def fattn_bwd_dq(q, k, v, dO, lse, dvec, dq, B, H, N, d, scale, causal, dtype, stream=None) -> int:
     return lib().fattn_bwd_dq(q, k, v, dO, lse, dvec, dq, B, H, N, d, scale, causal, dtype, stream)
+
+
+def fattn_splitkv_num_splits(B, H, Nq, Nk, d) -> int:
+    return lib().fattn_splitkv_num_splits(B, H, Nq, Nk, d)
+
+
+def fattn_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, num_splits) -> int:
+    return lib().fattn_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, num_splits)
+
+
+def fattn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num_splits,
+                      workspace, workspace_bytes, stream=None) -> int:
+    return lib().fattn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num_splits,
+                                   workspace, workspace_bytes, stream)
+
+
+def fattn_fwd_partial(q, k, v, o_parts, lse_parts, B, H, Nq, Nk, d, scale, causal, dtype, num_splits,
+                      stream=None) -> int:
+    return lib().fattn_fwd_partial(q, k, v, o_parts, lse_parts, B, H, Nq, Nk, d, scale, causal, dtype,
+                                   num_splits, stream)
+
+
+def fattn_combine(o_parts, lse_parts, num_splits, o, lse, B, H, Nq, d, dtype, stream=None) -> int:
+    return lib().fattn_combine(o_parts, lse_parts, num_splits, o, lse, B, H, Nq, d, dtype, stream)
 
 
 def fattn_strerror(status: int) -> str:
@@ -224,3 +262,96 @@ def backward_stages(q, k, v, o, do, lse, dq, dk, dv, dvec, causal=False, scale=N
             raise ValueError(f"unknown backward stage {stage}")
         if st != 0:
             raise FattnError(st, f"backward stage {stage}")
+
+
+def _check_dev(t, name, shape=None, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+
+
+def _decode_shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _check_dev(q, "q")
+    _check_dev(k, "k", (B, H, Nk, d), q.dtype)
+    _check_dev(v, "v", (B, H, Nk, d), q.dtype)
+    return B, H, Nq, Nk, d
+
+
+def forward_splitkv(q, k, v, causal=False, scale=None, num_splits=0, out=None, lse=None,
+                    workspace=None, stream=None):
+    """O [B, H, Nq, d], LSE [B, H, Nq] of q [B, H, Nq, d] against k, v [B, H, Nk, d] by split-KV
+    partials and their merge (float16/bfloat16). ``num_splits`` 0 lets the library choose."""
+    import torch
+    B, H, Nq, Nk, d = _decode_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fattn_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, int(num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_dev(out, "out", q.shape, q.dtype)
+    _check_dev(lse, "lse", (B, H, Nq), torch.float32)
+    st = fattn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                           B, H, Nq, Nk, d, float(scale), int(bool(causal)), dtype_code(q), int(num_splits),
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           _stream(stream))
+    if st != 0:
+        raise FattnError(st, "fattn_fwd_splitkv")
+    return out, lse
+
+
+def forward_partial(q, k, v, num_splits, causal=False, scale=None, o_parts=None, lse_parts=None,
+                    stream=None):
+    """Per-split partials O_s [S, B, H, Nq, d] and LSE_s [S, B, H, Nq] (float32)."""
+    import torch
+    B, H, Nq, Nk, d = _decode_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    S = int(num_splits)
+    if o_parts is None:
+        o_parts = torch.empty((S, B, H, Nq, d), dtype=torch.float32, device=q.device)
+    if lse_parts is None:
+        lse_parts = torch.empty((S, B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_dev(o_parts, "o_parts", (S, B, H, Nq, d), torch.float32)
+    _check_dev(lse_parts, "lse_parts", (S, B, H, Nq), torch.float32)
+    st = fattn_fwd_partial(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_parts.data_ptr(),
+                           lse_parts.data_ptr(), B, H, Nq, Nk, d, float(scale), int(bool(causal)),
+                           dtype_code(q), S, _stream(stream))
+    if st != 0:
+        raise FattnError(st, "fattn_fwd_partial")
+    return o_parts, lse_parts
+
+
+def combine(o_parts, lse_parts, dtype=None, out=None, lse=None, stream=None):
+    """Merge float32 partials O_s [S, B, H, Nq, d], LSE_s [S, B, H, Nq] into O (``dtype``, default
+    float32) and LSE [B, H, Nq]."""
+    import torch
+    if o_parts.dim() != 5:
+        raise ValueError("o_parts must be [S, B, H, Nq, d]")
+    S, B, H, Nq, d = o_parts.shape
+    _check_dev(o_parts, "o_parts", None, torch.float32)
+    _check_dev(lse_parts, "lse_parts", (S, B, H, Nq), torch.float32)
+    dtype = torch.float32 if dtype is None else dtype
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=dtype, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=o_parts.device)
+    _check_dev(out, "out", (B, H, Nq, d))
+    _check_dev(lse, "lse", (B, H, Nq), torch.float32)
+    st = fattn_combine(o_parts.data_ptr(), lse_parts.data_ptr(), S, out.data_ptr(), lse.data_ptr(),
+                       B, H, Nq, d, dtype_code(out), _stream(stream))
+    if st != 0:
+        raise FattnError(st, "fattn_combine")
+    return out, lse

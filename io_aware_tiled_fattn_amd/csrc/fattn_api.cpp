@@ -30,6 +30,42 @@ int check_common(int B, int H, int N, int d, int dtype) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? FATTN_OK : FATTN_ERR_LAUNCH; }
 
+constexpr int kMaxSplits = 1024;
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Shapes of the split-KV entry points: q [B,H,Nq,d], k/v [B,H,Nk,d], partials [S,B,H,Nq,d].
+int check_split_shape(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  if (d != 64 && d != 128) return FATTN_ERR_HEADDIM;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || Nq > kMaxN || Nk > kMaxN) return FATTN_ERR_SHAPE;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FATTN_ERR_SHAPE;
+  const long long bh = (long long)B * H;
+  if (bh > (1LL << 31) - 1) return FATTN_ERR_SHAPE;
+  if (bh * Nk > kMaxElems / d) return FATTN_ERR_SHAPE;
+  if (bh * Nq * num_splits > kMaxElems / d) return FATTN_ERR_SHAPE;
+  // partial-kernel grid: B*H*ceil(Nq/32)*S blocks
+  if (bh * ((Nq + 31) / 32) * num_splits > 0x7fffffffLL) return FATTN_ERR_SHAPE;
+  return FATTN_OK;
+}
+
+// Splits for num_splits = 0: enough work-groups to fill the chip several times over (about 2048),
+// but at least 256 keys per split so each work-group's pipeline runs for several tiles.
+int auto_splits(int B, int H, int Nq, int Nk) {
+  const long long wgs = (long long)B * H * ((Nq + 31) / 32);
+  long long s = (2048 + wgs - 1) / wgs;
+  const long long useful = ((long long)Nk + 255) / 256;
+  if (s > useful) s = useful;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : (int)s;
+}
+
+size_t split_o_bytes(int B, int H, int Nq, int d, int S) {
+  return round256((size_t)S * B * H * Nq * d * sizeof(float));
+}
+size_t split_lse_bytes(int B, int H, int Nq, int S) {
+  return round256((size_t)S * B * H * Nq * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -191,6 +227,100 @@ int fattn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, co
   fattn::BwdReq r{q, k, v, nullptr, dO, lse, dq, nullptr, nullptr, B, H, N, d, scale, causal, dtype,
                   (float*)dvec};
   return launch_status(fattn::launch_bwd(r, (hipStream_t)stream, 2));
+}
+
+int fattn_splitkv_num_splits(int B, int H, int Nq, int Nk, int d) {
+  if (check_split_shape(B, H, Nq, Nk, d, 1) != FATTN_OK) return 0;
+  return auto_splits(B, H, Nq, Nk);
+}
+
+size_t fattn_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  if (num_splits == 0 && check_split_shape(B, H, Nq, Nk, d, 1) == FATTN_OK)
+    num_splits = auto_splits(B, H, Nq, Nk);
+  if (check_split_shape(B, H, Nq, Nk, d, num_splits) != FATTN_OK) return 0;
+  return split_o_bytes(B, H, Nq, d, num_splits) + split_lse_bytes(B, H, Nq, num_splits);
+}
+
+static int check_partial(const void* q, const void* k, const void* v, const void* o_parts,
+                         const void* lse_parts, int B, int H, int Nq, int Nk, int d, float scale,
+                         int causal, int dtype, int num_splits) {
+  if (!q || !k || !v || !o_parts || !lse_parts) return FATTN_ERR_NULL;
+  if (dtype != FATTN_F16 && dtype != FATTN_BF16) return FATTN_ERR_DTYPE;
+  int st = check_split_shape(B, H, Nq, Nk, d, num_splits);
+  if (st != FATTN_OK) return st;
+  if (causal != 0 && causal != 1) return FATTN_ERR_CAUSAL;
+  if (causal && Nq > Nk) return FATTN_ERR_SHAPE;
+  if (!std::isfinite(scale)) return FATTN_ERR_SCALE;
+  const void* ins[3] = {q, k, v};
+  for (const void* p : ins) {
+    if (!aligned16(p)) return FATTN_ERR_ALIGN;
+    if (p == o_parts || p == lse_parts) return FATTN_ERR_ALIAS;
+  }
+  if (!aligned16(o_parts) || !aligned16(lse_parts)) return FATTN_ERR_ALIGN;
+  if (o_parts == lse_parts) return FATTN_ERR_ALIAS;
+  return FATTN_OK;
+}
+
+static int check_combine(const float* o_parts, const float* lse_parts, int num_splits, const void* o,
+                         const float* lse, int B, int H, int Nq, int d, int dtype) {
+  if (!o_parts || !lse_parts || !o || !lse) return FATTN_ERR_NULL;
+  if (dtype != FATTN_F32 && dtype != FATTN_F16 && dtype != FATTN_BF16) return FATTN_ERR_DTYPE;
+  int st = check_split_shape(B, H, Nq, 1, d, num_splits);
+  if (st != FATTN_OK) return st;
+  if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse))
+    return FATTN_ERR_ALIGN;
+  const void* ins[2] = {o_parts, lse_parts};
+  for (const void* p : ins)
+    if (p == o || p == (const void*)lse) return FATTN_ERR_ALIAS;
+  if (o == (const void*)lse) return FATTN_ERR_ALIAS;
+  return FATTN_OK;
+}
+
+int fattn_fwd_partial(const void* q, const void* k, const void* v, float* o_parts, float* lse_parts,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                      int num_splits, void* stream) {
+  int st = check_partial(q, k, v, o_parts, lse_parts, B, H, Nq, Nk, d, scale, causal, dtype, num_splits);
+  if (st != FATTN_OK) return st;
+  fattn::SplitReq r{q, k, v, o_parts, lse_parts, B, H, Nq, Nk, d, scale, causal, dtype, num_splits};
+  return launch_status(fattn::launch_splitkv_partial(r, (hipStream_t)stream));
+}
+
+int fattn_combine(const float* o_parts, const float* lse_parts, int num_splits, void* o, float* lse,
+                  int B, int H, int Nq, int d, int dtype, void* stream) {
+  int st = check_combine(o_parts, lse_parts, num_splits, o, lse, B, H, Nq, d, dtype);
+  if (st != FATTN_OK) return st;
+  fattn::CombineReq r{o_parts, lse_parts, o, lse, B, H, Nq, d, dtype, num_splits};
+  return launch_status(fattn::launch_combine(r, (hipStream_t)stream));
+}
+
+int fattn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                      int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FATTN_ERR_NULL;
+  if (dtype != FATTN_F16 && dtype != FATTN_BF16) return FATTN_ERR_DTYPE;
+  if (num_splits == 0 && check_split_shape(B, H, Nq, Nk, d, 1) == FATTN_OK)
+    num_splits = auto_splits(B, H, Nq, Nk);
+  int st = check_split_shape(B, H, Nq, Nk, d, num_splits);
+  if (st != FATTN_OK) return st;
+  if (causal != 0 && causal != 1) return FATTN_ERR_CAUSAL;
+  if (causal && Nq > Nk) return FATTN_ERR_SHAPE;
+  if (!std::isfinite(scale)) return FATTN_ERR_SCALE;
+  const size_t ob = split_o_bytes(B, H, Nq, d, num_splits);
+  if (!workspace || workspace_bytes < ob + split_lse_bytes(B, H, Nq, num_splits))
+    return FATTN_ERR_WORKSPACE;
+  const void* all[6] = {q, k, v, o, lse, workspace};
+  for (const void* p : all)
+    if (!aligned16(p)) return FATTN_ERR_ALIGN;
+  for (int i = 3; i < 6; ++i)
+    for (int j = 0; j < 6; ++j)
+      if (i != j && all[i] == all[j]) return FATTN_ERR_ALIAS;
+  float* o_parts = (float*)workspace;
+  float* lse_parts = (float*)((char*)workspace + ob);
+  fattn::SplitReq r{q, k, v, o_parts, lse_parts, B, H, Nq, Nk, d, scale, causal, dtype, num_splits};
+  hipError_t e = fattn::launch_splitkv_partial(r, (hipStream_t)stream);
+  if (e != hipSuccess) return FATTN_ERR_LAUNCH;
+  fattn::CombineReq c{o_parts, lse_parts, o, lse, B, H, Nq, d, dtype, num_splits};
+  return launch_status(fattn::launch_combine(c, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -47,4 +47,33 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d);
 // 4 = dK pass only; -1 = preprocess, dK/dV, dQ in order
 hipError_t launch_bwd(const BwdReq& r, hipStream_t stream, int stage = -1);
 
+// Split-KV forward (query rows Nq against Nk keys, the keys cut into num_splits ranges).
+struct SplitReq {
+  const void* q;     // [B, H, Nq, d]
+  const void* k;     // [B, H, Nk, d]
+  const void* v;
+  float* o_part;     // [num_splits, B, H, Nq, d] float32
+  float* lse_part;   // [num_splits, B, H, Nq] float32
+  int B, H, Nq, Nk, d;
+  float scale;
+  int causal;
+  int dtype;
+  int num_splits;    // >= 1
+};
+struct CombineReq {
+  const float* o_part;
+  const float* lse_part;
+  void* o;           // [B, H, Nq, d] in dtype
+  float* lse;        // [B, H, Nq]
+  int B, H, Nq, d;
+  int dtype;
+  int num_splits;
+};
+// Split s covers keys [s * L, min(Nk, (s + 1) * L)) with L = splitkv_split_len(Nk, S), the
+// smallest multiple of kSplitAlign that is >= Nk / S.
+constexpr int kSplitAlign = 64;
+int splitkv_split_len(int Nk, int num_splits);
+hipError_t launch_splitkv_partial(const SplitReq& r, hipStream_t stream);
+hipError_t launch_combine(const CombineReq& r, hipStream_t stream);
+
 }  // namespace fattn

@@ -34,7 +34,9 @@ def test_every_declared_symbol_is_exported(L):
     names = _declared()
     assert {"fattn_fwd", "fattn_fwd_tiled", "fattn_bwd", "fattn_bwd_workspace_size",
             "fattn_strerror", "fattn_version", "fattn_bwd_preprocess", "fattn_bwd_dkdv",
-            "fattn_bwd_dv", "fattn_bwd_dk", "fattn_bwd_dq"} <= set(names)
+            "fattn_bwd_dv", "fattn_bwd_dk", "fattn_bwd_dq", "fattn_fwd_splitkv",
+            "fattn_fwd_splitkv_workspace_size", "fattn_splitkv_num_splits", "fattn_fwd_partial",
+            "fattn_combine"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
         assert getattr(fa, n) is not None
@@ -139,4 +141,71 @@ def test_binding_refuses_host_tensors():
     (lambda: fa.fattn_bwd_dk(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 1, 1, 8, 64, 0.1, 0, 0), -4),
 ])
 def test_backward_stages_reject_bad_arguments(L, call, status):
+    assert call() == status
+
+
+# --------------------------------------------------------------------------------------------
+# Split-KV entry points
+
+
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
+def test_splitkv_sizes(L):
+    S = fa.fattn_splitkv_num_splits(8, 32, 1, 16384, 128)
+    assert 1 <= S <= 1024
+    # a head-rich shape needs no splitting beyond what fills the chip; tiny Nk cannot be split
+    assert fa.fattn_splitkv_num_splits(64, 64, 1, 16384, 128) >= 1
+    assert fa.fattn_splitkv_num_splits(1, 1, 1, 100, 128) == 1
+    assert fa.fattn_splitkv_num_splits(1, 1, 1, 100, 96) == 0
+    for B, H, nq, nk, d, s in [(8, 32, 1, 16384, 128, 8), (2, 3, 40, 1000, 64, 5), (1, 1, 1, 1, 64, 1)]:
+        n = fa.fattn_fwd_splitkv_workspace_size(B, H, nq, nk, d, s)
+        assert n == _r256(s * B * H * nq * d * 4) + _r256(s * B * H * nq * 4)
+    auto = fa.fattn_splitkv_num_splits(8, 32, 16, 16384, 128)
+    assert fa.fattn_fwd_splitkv_workspace_size(8, 32, 16, 16384, 128, 0) == \
+        fa.fattn_fwd_splitkv_workspace_size(8, 32, 16, 16384, 128, auto)
+    assert fa.fattn_fwd_splitkv_workspace_size(8, 32, 16, 16384, 128, 1025) == 0
+    assert fa.fattn_fwd_splitkv_workspace_size(8, 32, 0, 16384, 128, 4) == 0
+
+
+def split(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, Nq=4, Nk=100, d=64, scale=0.125,
+             causal=0, dtype=fa.FATTN_BF16, S=2, ws=P[5], wsb=1 << 20, stream=None)
+    a.update(kw)
+    return fa.fattn_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                                a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], a["S"], a["ws"],
+                                a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(v=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+    (dict(dtype=fa.FATTN_F32), -4), (dict(dtype=7), -4), (dict(d=96), -3),
+    (dict(Nq=0), -2), (dict(Nk=0), -2), (dict(B=0), -2), (dict(S=1025), -2), (dict(S=-1), -2),
+    (dict(causal=1, Nq=101), -2), (dict(causal=3), -12), (dict(scale=float("inf")), -7),
+    (dict(ws=None), -8), (dict(wsb=100), -8), (dict(q=MIS), -6), (dict(ws=MIS), -6),
+    (dict(o=P[0]), -11), (dict(lse=P[1]), -11), (dict(ws=P[3]), -11), (dict(o=P[4]), -11),
+    (dict(Nq=16777217), -2),
+])
+def test_splitkv_rejects_bad_arguments(L, kw, status):
+    assert split(**kw) == status
+
+
+@pytest.mark.parametrize("call,status", [
+    (lambda: fa.fattn_fwd_partial(P[0], P[1], P[2], None, P[4], 1, 1, 4, 100, 64, 0.1, 0, 2, 2), -1),
+    (lambda: fa.fattn_fwd_partial(P[0], P[1], P[2], P[3], P[4], 1, 1, 4, 100, 64, 0.1, 0, 2, 0), -2),
+    (lambda: fa.fattn_fwd_partial(P[0], P[1], P[2], P[3], P[3], 1, 1, 4, 100, 64, 0.1, 0, 2, 2), -11),
+    (lambda: fa.fattn_fwd_partial(P[0], P[1], P[2], P[0], P[4], 1, 1, 4, 100, 64, 0.1, 0, 2, 2), -11),
+    (lambda: fa.fattn_fwd_partial(P[0], P[1], P[2], P[3], MIS, 1, 1, 4, 100, 64, 0.1, 0, 2, 2), -6),
+    (lambda: fa.fattn_fwd_partial(P[0], P[1], P[2], P[3], P[4], 1, 1, 4, 100, 64, 0.1, 0, 0, 2), -4),
+    (lambda: fa.fattn_fwd_partial(P[0], P[1], P[2], P[3], P[4], 1, 1, 200, 100, 64, 0.1, 1, 2, 2), -2),
+    (lambda: fa.fattn_combine(None, P[1], 2, P[2], P[3], 1, 1, 4, 64, 2), -1),
+    (lambda: fa.fattn_combine(P[0], P[1], 0, P[2], P[3], 1, 1, 4, 64, 2), -2),
+    (lambda: fa.fattn_combine(P[0], P[1], 2, P[0], P[3], 1, 1, 4, 64, 2), -11),
+    (lambda: fa.fattn_combine(P[0], P[1], 2, P[2], P[2], 1, 1, 4, 64, 2), -11),
+    (lambda: fa.fattn_combine(P[0], P[1], 2, P[2], P[3], 1, 1, 4, 64, 9), -4),
+    (lambda: fa.fattn_combine(P[0], P[1], 2, P[2], P[3], 1, 1, 4, 80, 0), -3),
+    (lambda: fa.fattn_combine(P[0], MIS, 2, P[2], P[3], 1, 1, 4, 64, 0), -6),
+])
+def test_partial_and_combine_reject_bad_arguments(L, call, status):
     assert call() == status
