@@ -4,7 +4,8 @@ A step is one pass of the whole hot path over one batch: fattn_fwd then fattn_bw
 dK/dV, dQ) on the training-shaped workload B=2, H=16, N=4096, d=128 (causal, bf16; Q, K, V, dO
 iid N(0,1) from a seed). FLOPs per step follow the stated convention: forward 4*B*H*N^2*d halved
 for causal, backward 2.5x the forward. The forward alone is also timed on the prefill workload
-B=4, H=16, N=4096.
+B=4, H=16, N=4096, and the split-KV forward on the decode workloads (B=8, H=32, d=128, one or
+16 queries per head against a 16384-key cache), reported in GB/s against the HBM peak.
 
 Timing: HIP events on the stream the kernels are launched on (torch's current stream), after
 warm-up, inputs resident in HBM. Every kernel of the step is also timed on its own (one launch
@@ -41,6 +42,12 @@ def _upload(inp, torch):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
     return tuple(up(inp.bits[n]) if n in inp.bits else None for n in ("q", "k", "v", "do"))
+
+
+def _upload_named(inp, names, torch):
+    import numpy as np
+    return tuple(torch.from_numpy(np.ascontiguousarray(inp.bits[n]).view(np.int16)).view(torch.bfloat16).cuda()
+                 for n in names)
 
 
 def _time_calls(fn, steps, warmup, torch, min_warm_s=0.05):
@@ -101,6 +108,8 @@ def main(argv=None):
     ap.add_argument("--clock-warmup-s", type=float, default=1.0,
                     help="seconds of untimed fwd+bwd steps before any timing, to reach steady clocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", default="6,7",
+                    help="split-KV decode workloads to time (comma-separated ids, or 'none')")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB read + 256 MiB write elementwise copy, so HBM "
                          "byte counters can be scaled by a kernel of known traffic")
@@ -135,6 +144,24 @@ def main(argv=None):
     del inp3
     o3, l3 = fa.forward(q3, k3, v3, causal=True)
 
+    # Decode workloads: one key/value cache shared by both, each with its own queries.
+    dec = {}
+    dec_ids = [] if a.decode == "none" else [int(x) for x in a.decode.split(",")]
+    if dec_ids:
+        kv = fi.decode_workload_inputs(dec_ids[0], with_q=False)
+        kc, vc = _upload_named(kv, ("k", "v"), torch)
+        del kv
+        for ident in dec_ids:
+            wd = fi.DECODE_WORKLOADS[ident]
+            (qd,) = _upload_named(fi.decode_workload_inputs(ident, with_kv=False), ("q",), torch)
+            S = fa.fattn_splitkv_num_splits(wd.B, wd.H, wd.Nq, wd.Nk, wd.d)
+            wsd = torch.empty(fa.fattn_fwd_splitkv_workspace_size(wd.B, wd.H, wd.Nq, wd.Nk, wd.d, S),
+                              dtype=torch.uint8, device="cuda")
+            od, ld = fa.forward_splitkv(qd, kc, vc, causal=True, num_splits=S, workspace=wsd)
+            op = torch.empty((S, wd.B, wd.H, wd.Nq, wd.d), dtype=torch.float32, device="cuda")
+            lp = torch.empty((S, wd.B, wd.H, wd.Nq), dtype=torch.float32, device="cuda")
+            dec[ident] = (wd, qd, S, wsd, od, ld, op, lp)
+
     # Bring the GPU to its steady clock before anything is timed: the engine clock ramps up over
     # the first few hundred milliseconds of sustained MFMA work, and a short warm-up under-reports.
     def step():
@@ -166,6 +193,48 @@ def main(argv=None):
     ms_fwd3 = T(lambda: fa.forward(q3, k3, v3, causal=True, out=o3, lse=l3))
     del q3, k3, v3, o3, l3
 
+    tr_all = profiling.load_traffic(os.path.join(ROOT, "profiles"))
+
+    # Split-KV decode: whole path (partials + merge), and each kernel on its own.
+    decode = {}
+    for ident, (wd, qd, S, wsd, od, ld, op, lp) in dec.items():
+        causal = True  # with the queries at the end of the sequence (bottom-right alignment)
+        t_all = T(lambda: fa.forward_splitkv(qd, kc, vc, causal=causal, num_splits=S, out=od, lse=ld,
+                                             workspace=wsd))
+        t_part = T(lambda: fa.forward_partial(qd, kc, vc, S, causal=causal, o_parts=op, lse_parts=lp))
+        t_comb = T(lambda: fa.combine(op, lp, dtype=torch.bfloat16, out=od, lse=ld))
+        bh = wd.B * wd.H
+        kv_b = 2 * bh * wd.Nk * wd.d * 2
+        q_b = bh * wd.Nq * wd.d * 2
+        out_b = bh * wd.Nq * (wd.d * 2 + 4)
+        part_b = S * bh * wd.Nq * (wd.d + 1) * 4
+        gbs = lambda nbytes, t_ms: nbytes / (t_ms * 1e-3) / 1e9
+        dtraffic = None
+        if tr_all:
+            sig_d = "splitkv_kernel<Bf16, 128, 32, 3, true, false>"
+            grid_d = bh * ((wd.Nq + 31) // 32) * S * 64
+            for (kname, kgrid), rec in tr_all.items():
+                if kname.startswith(sig_d) and kgrid == grid_d and ident == 6:
+                    dtraffic = {"fetch_bytes": round(rec["fetch_bytes"]), "write_bytes": round(rec["write_bytes"]),
+                                "source": "profiles/traffic.json"}
+        path_gbs = gbs(kv_b + q_b + out_b, t_all)
+        part_gbs = gbs(kv_b + q_b + part_b, t_part)
+        decode[f"w{ident}"] = {
+            "workload": f"{wd.name}: B={wd.B} H={wd.H} Nq={wd.Nq} Nk={wd.Nk} d={wd.d} causal",
+            "num_splits": S, "ms": round(t_all, 4), "GB_s": round(path_gbs, 1),
+            "frac_of_hbm_peak": round(path_gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": kv_b + q_b + out_b,
+            "kernel_ms": {"partial": round(t_part, 4), "combine": round(t_comb, 4)},
+            "roofline": {"kernel": "splitkv_kernel (partials)", "bound": "hbm",
+                         "achieved": round(part_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(part_gbs / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes_per_launch": kv_b + q_b + part_b, "traffic": dtraffic,
+                         "ms_per_launch": round(t_part, 4)},
+        }
+    dec.clear()
+    if dec_ids:
+        del kc, vc
+
     if a.calibrate_copy:
         src = torch.ones(128 * 2**20, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
@@ -192,9 +261,8 @@ def main(argv=None):
     name, fl, grid, sig = kernels[dom]
     achieved = tf(fl, ms[dom])
     traffic = None
-    tr = profiling.load_traffic(os.path.join(ROOT, "profiles"))
-    if tr:
-        for (kname, kgrid), rec in tr.items():
+    if tr_all:
+        for (kname, kgrid), rec in tr_all.items():
             if kname.startswith(sig) and kgrid == grid:
                 traffic = {"fetch_bytes": round(rec["fetch_bytes"]), "write_bytes": round(rec["write_bytes"]),
                            "source": "profiles/traffic.json"}
@@ -228,6 +296,8 @@ def main(argv=None):
         "kernel_ms": {k_: round(t, 4) for k_, t in ms.items()},
         "roofline": roof,
     }
+    if decode:
+        result["decode"] = decode
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_oracle_baseline()
     print(json.dumps(result), flush=True)

@@ -69,6 +69,7 @@ class DecodeWorkload:
     Nq: int
     Nk: int
     d: int
+    kv_seed: int  # seed of the key/value cache draw (shared by workloads over the same cache)
 
     @property
     def scale(self) -> float:
@@ -76,10 +77,10 @@ class DecodeWorkload:
 
 
 # Split-KV forward workloads: one query per head (token-by-token decode) and 16 (a block of
-# draft tokens checked at once), both over a 16384-key cache at d = 128.
+# draft tokens checked at once), both over the same 16384-key cache at d = 128.
 DECODE_WORKLOADS = {
-    6: DecodeWorkload(6, "decode bf16 split-KV forward", "bf16", 8, 32, 1, 16384, 128),
-    7: DecodeWorkload(7, "multi-token decode bf16 split-KV forward", "bf16", 8, 32, 16, 16384, 128),
+    6: DecodeWorkload(6, "decode bf16 split-KV forward", "bf16", 8, 32, 1, 16384, 128, 6),
+    7: DecodeWorkload(7, "multi-token decode bf16 split-KV forward", "bf16", 8, 32, 16, 16384, 128, 6),
 }
 
 # Variants: 0 = base draw; 1 = every logit shifted by exactly +500 (Q[...,0] = 1 and
@@ -101,13 +102,14 @@ def round_bits(x: np.ndarray, dtype: str):
         h = x.astype(np.float16)  # numpy's float32->float16 cast is round-to-nearest-even
         return h.astype(np.float32), h.view(np.uint16)
     if dtype == "bf16":
-        u = x.view(np.uint32).astype(np.uint64)
         if not np.all(np.isfinite(x)):
             raise ValueError("bf16 rounding expects finite inputs")
-        lsb = (u >> 16) & 1
-        r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint32)
+        # finite floats have bits <= 0xFF7FFFFF, so adding at most 0x8000 stays within 32 bits
+        u = x.view(np.uint32)
+        r = (u + ((u >> 16) & np.uint32(1)) + np.uint32(0x7FFF)) >> 16
         bits = r.astype(np.uint16)
-        vals = (r << 16).astype(np.uint32).view(np.float32)
+        r <<= 16
+        vals = r.view(np.float32)
         return vals, bits
     raise ValueError(f"unknown dtype {dtype!r}")
 
@@ -160,12 +162,28 @@ def make_inputs(shape, dtype: str, seed: int, variant: int = VARIANT_BASE, with_
     return Inputs(dtype, q, k, v, do, bits)
 
 
-def make_decode_inputs(B, H, nq, nk, d, dtype: str, seed: int, variant: int = VARIANT_BASE) -> Inputs:
-    """Seeded Q [B, H, nq, d] and K, V [B, H, nk, d], rounded to ``dtype`` (no dO)."""
-    q, qb = draw((B, H, nq, d), (seed, variant, _Q), dtype)
-    k, kb = draw((B, H, nk, d), (seed, variant, _K), dtype)
-    v, vb = draw((B, H, nk, d), (seed, variant, _V), dtype)
+def make_decode_inputs(B, H, nq, nk, d, dtype: str, seed: int, variant: int = VARIANT_BASE,
+                       kv_seed: int | None = None, with_q: bool = True, with_kv: bool = True) -> Inputs:
+    """Seeded Q [B, H, nq, d] and K, V [B, H, nk, d], rounded to ``dtype`` (no dO).
+
+    K and V come from ``kv_seed`` (default ``seed``); ``with_q`` / ``with_kv`` = False skip a
+    draw (the field is then None), so a shared cache is drawn once.
+    """
+    kv_seed = seed if kv_seed is None else kv_seed
+    q = qb = k = kb = v = vb = None
+    if with_q:
+        q, qb = draw((B, H, nq, d), (seed, variant, _Q), dtype)
+    if with_kv:
+        k, kb = draw((B, H, nk, d), (kv_seed, variant, _K), dtype)
+        v, vb = draw((B, H, nk, d), (kv_seed, variant, _V), dtype)
     return Inputs(dtype, q, k, v, None, {"q": qb, "k": kb, "v": vb})
+
+
+def decode_workload_inputs(ident: int, with_q: bool = True, with_kv: bool = True) -> Inputs:
+    """Inputs of decode workload ``ident`` (6, 7) at full size."""
+    w = DECODE_WORKLOADS[ident]
+    return make_decode_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, ident, kv_seed=w.kv_seed,
+                              with_q=with_q, with_kv=with_kv)
 
 
 def unshifted_partner(inp: Inputs, scale: float) -> Inputs:

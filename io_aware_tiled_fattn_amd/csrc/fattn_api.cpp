@@ -48,11 +48,12 @@ int check_split_shape(int B, int H, int Nq, int Nk, int d, int num_splits) {
   return FATTN_OK;
 }
 
-// Splits for num_splits = 0: enough work-groups to fill the chip several times over (about 2048),
-// but at least 256 keys per split so each work-group's pipeline runs for several tiles.
+// Splits for num_splits = 0: about 1024 work-groups, i.e. two full rounds of the partial kernel's
+// resident work-groups (two per CU on 256 CUs at d = 128), but at least 256 keys per split so each
+// work-group's pipeline runs for several tiles.
 int auto_splits(int B, int H, int Nq, int Nk) {
   const long long wgs = (long long)B * H * ((Nq + 31) / 32);
-  long long s = (2048 + wgs - 1) / wgs;
+  long long s = (1024 + wgs - 1) / wgs;
   const long long useful = ((long long)Nk + 255) / 256;
   if (s > useful) s = useful;
   if (s > kMaxSplits) s = kMaxSplits;

@@ -19,7 +19,8 @@
 // from LDS with ds_read_b128, V with ds_read_b64_tr_b16). K/V tiles of BC keys go from memory
 // straight into LDS (buffer_load ... lds), NS stages deep, so NS - 1 tiles per wave are in flight
 // while one is computed. With one wave per work-group the LDS budget, not the register file,
-// sets how many tiles a CU keeps in flight.
+// sets how many tiles a CU keeps in flight; the kernel is bound by HBM bandwidth, and the MFMA
+// work (32 query rows per tile even for one real query) stays far below its own bound.
 //
 // Causal with Nq queries and Nk keys: query i is position i + Nk - Nq of the sequence and sees
 // keys j <= i + Nk - Nq (with Nq == Nk, the ordinary causal mask).
@@ -372,9 +373,11 @@ int splitkv_split_len(int Nk, int num_splits) {
 }
 
 hipError_t launch_splitkv_partial(const SplitReq& r, hipStream_t st) {
+  // 32-key tiles, four stages: three tiles per wave in flight (64 KiB of LDS at d = 128, two
+  // work-groups per CU). Measured against 32/64-key tiles with 2..5 stages on the decode shapes.
   if (r.dtype == FATTN_BF16)
-    return r.d == 64 ? launch_split_t<Bf16, 64, 32, 3>(r, st) : launch_split_t<Bf16, 128, 32, 3>(r, st);
-  return r.d == 64 ? launch_split_t<F16, 64, 32, 3>(r, st) : launch_split_t<F16, 128, 32, 3>(r, st);
+    return r.d == 64 ? launch_split_t<Bf16, 64, 32, 4>(r, st) : launch_split_t<Bf16, 128, 32, 4>(r, st);
+  return r.d == 64 ? launch_split_t<F16, 64, 32, 4>(r, st) : launch_split_t<F16, 128, 32, 4>(r, st);
 }
 
 hipError_t launch_combine(const CombineReq& r, hipStream_t st) {

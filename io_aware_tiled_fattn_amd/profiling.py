@@ -22,7 +22,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-KERNEL_SOURCES = ("fattn_device.hpp", "fattn_fwd.hip", "fattn_bwd.hip")
+KERNEL_SOURCES = ("fattn_device.hpp", "fattn_fwd.hip", "fattn_bwd.hip", "fattn_splitkv.hip")
+DECODE_KERNELS = ("splitkv_kernel", "combine_kernel")
 COPY_BYTES = 256 * 2**20  # the calibration copy reads and writes this many bytes each
 
 COMMANDS = {
@@ -30,10 +31,10 @@ COMMANDS = {
              "python -u bench.py --steps 10 --warmup 3 --no-cpu-baseline --clock-warmup-s 0.5",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {run}/fetch -o run -- "
              "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy "
-             "--clock-warmup-s 0",
+             "--clock-warmup-s 0 --decode 6",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {run}/write -o run -- "
              "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy "
-             "--clock-warmup-s 0",
+             "--clock-warmup-s 0 --decode 6",
 }
 
 
@@ -48,7 +49,8 @@ def source_hash() -> str:
 def short_name(kernel: str) -> str:
     k = kernel.replace("fattn::(anonymous namespace)::", "").replace("fattn::", "")
     k = k.replace("(unsigned short const*, unsigned short const*, float*, long long)", "")
-    k = k.replace("((anonymous namespace)::FwdArgs)", "").replace("((anonymous namespace)::BwdArgs)", "")
+    for args in ("FwdArgs", "BwdArgs", "SplitArgs", "CombineArgs"):
+        k = k.replace(f"((anonymous namespace)::{args})", "")
     return k.replace("void ", "").strip()
 
 
@@ -116,34 +118,53 @@ def traffic(run_dir):
     return out, fc, wc
 
 
+def _is_decode(kernel):
+    return any(kernel.startswith(d) for d in DECODE_KERNELS)
+
+
+DECODE_WORKLOAD = "decode_b8h32nk16384d128_bf16"
+
+
 def write_summaries(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
     os.makedirs(prof_dir, exist_ok=True)
     stats = kernel_stats(run_dir)
-    cmd_note = "Commands (from the repository root, on the GPU box; RUN is an output folder):\n\n"
-    lines = [f"# Kernel times — bench.py step workload ({workload}) and the B=4 forward\n",
-             cmd_note + "    " + COMMANDS["trace"].format(run="RUN") + "\n",
-             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
-    for s in stats:
-        lines.append(f"| `{s['kernel']}` | {s['calls']} | {s['avg_us']:.1f} | {s['min_us']:.1f} | "
-                     f"{s['max_us']:.1f} | {s['pct']:.1f} |")
-    lines.append("\nThe forward kernel's calls mix the B=2 (step) and B=4 (prefill) workloads; "
-                 "bench.py times each live with HIP events.")
-    with open(os.path.join(prof_dir, f"kernel_times_{workload}.md"), "w") as f:
-        f.write("\n".join(lines) + "\n")
-
     tr, fc, wc = traffic(run_dir)
-    lines = [f"# HBM traffic per launch ({workload} and the B=4 forward)\n",
-             cmd_note + "    " + COMMANDS["fetch"].format(run="RUN") + "\n    " +
-             COMMANDS["write"].format(run="RUN") + "\n",
-             f"Calibration (elementwise copy, 256 MiB read + 256 MiB written): FETCH_SIZE reads "
-             f"{fc:.3f} x true bytes, WRITE_SIZE reads {wc:.3f} x; the figures below are divided by "
-             f"those factors.\n",
-             "| kernel | grid | fetched MiB | written MiB |", "|---|---|---|---|"]
-    for t in tr:
-        lines.append(f"| `{t['kernel']}` | {t['grid']} | {t['fetch_bytes'] / 2**20:.1f} | "
-                     f"{t['write_bytes'] / 2**20:.1f} |")
-    with open(os.path.join(prof_dir, f"hbm_traffic_{workload}.md"), "w") as f:
-        f.write("\n".join(lines) + "\n")
+    cmd_note = "Commands (from the repository root, on the GPU box; RUN is an output folder):\n\n"
+    titles = {
+        workload: (f"bench.py step workload ({workload}) and the B=4 forward",
+                   "The forward kernel's calls mix the B=2 (step) and B=4 (prefill) workloads; "
+                   "bench.py times each live with HIP events."),
+        DECODE_WORKLOAD: ("bench.py split-KV decode workloads (B=8 H=32 Nk=16384 d=128 bf16, "
+                          "Nq = 1 and Nq = 16, one shared cache)",
+                          "The partial kernel's calls mix Nq = 1 and Nq = 16 (same grid); the "
+                          "counter runs (HBM traffic) run the Nq = 1 workload only."),
+    }
+    for wl, (title, note) in titles.items():
+        pick = (lambda k: _is_decode(k)) if wl == DECODE_WORKLOAD else (lambda k: not _is_decode(k))
+        lines = [f"# Kernel times — {title}\n",
+                 cmd_note + "    " + COMMANDS["trace"].format(run="RUN") + "\n",
+                 "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+        for s in stats:
+            if pick(s["kernel"]):
+                lines.append(f"| `{s['kernel']}` | {s['calls']} | {s['avg_us']:.1f} | {s['min_us']:.1f} | "
+                             f"{s['max_us']:.1f} | {s['pct']:.1f} |")
+        lines.append("\n" + note + " % time is over every kernel of the run.")
+        with open(os.path.join(prof_dir, f"kernel_times_{wl}.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+
+        lines = [f"# HBM traffic per launch — {title}\n",
+                 cmd_note + "    " + COMMANDS["fetch"].format(run="RUN") + "\n    " +
+                 COMMANDS["write"].format(run="RUN") + "\n",
+                 f"Calibration (elementwise copy, 256 MiB read + 256 MiB written): FETCH_SIZE reads "
+                 f"{fc:.3f} x true bytes, WRITE_SIZE reads {wc:.3f} x; the figures below are divided by "
+                 f"those factors.\n",
+                 "| kernel | grid | fetched MiB | written MiB |", "|---|---|---|---|"]
+        for t in tr:
+            if pick(t["kernel"]):
+                lines.append(f"| `{t['kernel']}` | {t['grid']} | {t['fetch_bytes'] / 2**20:.1f} | "
+                             f"{t['write_bytes'] / 2**20:.1f} |")
+        with open(os.path.join(prof_dir, f"hbm_traffic_{wl}.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
     with open(os.path.join(prof_dir, "traffic.json"), "w") as f:
         json.dump({"source_hash": source_hash(), "fetch_factor": fc, "write_factor": wc,
                    "kernels": tr}, f, indent=1)

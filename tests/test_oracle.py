@@ -415,10 +415,12 @@ def test_bf16_and_f16_rounding_match_torch_bit_for_bit():
     torch = pytest.importorskip("torch")
     r = _rng(21)
     x = np.concatenate([r.standard_normal(100000).astype(np.float32) * s for s in (1, 1e-3, 300, 7e4)])
-    x = np.concatenate([x, np.array([1.00390625, 1.01171875, -2.0039062, 0.0, -0.0], np.float32)])
-    _, bb = fi.round_bits(x, "bf16")
+    x = np.concatenate([x, np.array([1.00390625, 1.01171875, -2.0039062, 0.0, -0.0,
+                                     3.4028235e38, -3.4028235e38, 3.3e38, 1e-45, -1e-40], np.float32)])
+    bv, bb = fi.round_bits(x, "bf16")
     tb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(bb, tb)
+    np.testing.assert_array_equal(bv, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
     xh = x[np.abs(x) < 6e4]
     _, hb = fi.round_bits(xh, "f16")
     th = torch.from_numpy(xh).to(torch.float16).view(torch.int16).numpy().view(np.uint16)

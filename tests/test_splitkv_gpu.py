@@ -191,7 +191,7 @@ def test_decode_workloads_sampled_heads(ident, causal):
     fa = _fa()
     w = fi.DECODE_WORKLOADS[ident]
     log(f"decode workload {ident} ({w.name}) causal={causal}")
-    inp = fi.make_decode_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, ident)
+    inp = fi.decode_workload_inputs(ident)
     q, k, v = _up(inp)
     o, lse = fa.forward_splitkv(q, k, v, causal=causal)
     _torch().cuda.synchronize()
