@@ -76,7 +76,8 @@ int fattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * fattn_fwd with an explicit tile shape: Br query rows per work-group, Bc key rows per step
  * (page 2, tips: the tile sizes change the on-chip working set, not the result). Br = Bc = 0
  * selects the default, so fattn_fwd(...) == fattn_fwd_tiled(..., 0, 0, stream).
- * Supported (Br, Bc): f16/bf16 — {64, 128} x {64, 128}; f32 — (128, 32) and (64, 32).
+ * Supported (Br, Bc): f16/bf16 — {64, 128, 256} x {64, 128}; f32 — (128, 32) and (64, 32).
+ * Defaults: f16/bf16 (256, 128) at d = 128 and (128, 64) at d = 64; f32 (128, 32).
  */
 int fattn_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int H, int N, int d, float scale, int causal, int dtype,

@@ -79,7 +79,7 @@ __device__ inline void fwd_block_coords(int bid, int nblocks, int n_qtiles, int 
   if (causal) *qt = n_qtiles - 1 - *qt;
 }
 
-template <int D, int BR, int BC>
+template <int D, int BR, int BC, int NS>
 struct FwdCfg {
   static constexpr int NW = BR / 32;          // waves per work-group
   static constexpr int NT = NW * 64;          // threads per work-group
@@ -87,16 +87,18 @@ struct FwdCfg {
   static constexpr int LPT = BC * CPR / NT;   // 16-byte loads per thread per tile per tensor
   static constexpr int TILE_B = BC * D * 2;   // bytes of one K (or V) tile
   static constexpr int STAGE_B = 2 * TILE_B;  // K then V
-  static constexpr int LDS_B = 2 * STAGE_B;   // two stages
+  static constexpr int LDS_B = NS * STAGE_B;  // NS stages: NS - 1 tiles in flight
+  static constexpr int LPI = 2 * LPT;         // load instructions per thread per tile
   static_assert(BC * CPR % NT == 0, "tile load split");
   static_assert(BR % 32 == 0 && BC % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert(NS >= 2 && (NS - 2) * LPI < 64, "vmcnt range");
 };
 
 // BIG: the head's K/V exceed the 32-bit range of buffer offsets, so tiles are fetched with
 // per-lane 64-bit global addresses instead.
-template <typename TR, int D, int BR, int BC, bool CAUSAL, bool BIG>
+template <typename TR, int D, int BR, int BC, int NS, bool CAUSAL, bool BIG>
 __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
-  using Cfg = FwdCfg<D, BR, BC>;
+  using Cfg = FwdCfg<D, BR, BC, NS>;
   using vec8 = typename TR::vec8;
   constexpr int NT = Cfg::NT, CPR = Cfg::CPR, LPT = Cfg::LPT, TILE_B = Cfg::TILE_B;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS_B];
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t rK = make_rsrc(Kh, head_bytes);
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(Vh, head_bytes);
   auto issue = [&](int j) {
-    uint8_t* st = smem + (j & 1) * Cfg::STAGE_B + w * 64 * 16;
+    uint8_t* st = smem + (j % NS) * Cfg::STAGE_B + w * 64 * 16;
     if (!BIG && (j + 1) * BC <= N) {
       const uint32_t soff = (uint32_t)(j * BC) * (D * 2);
 #pragma unroll
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   // ragged tiles; returns the row max of the log2-domain logits.
   auto scores = [&](int j, f32x16 (&s)[BC / 32]) {
     const int k0 = j * BC;
-    const uint8_t* Ks = smem + (j & 1) * Cfg::STAGE_B;
+    const uint8_t* Ks = smem + (j % NS) * Cfg::STAGE_B;
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   // fragments (8 keys per 16-key chunk), then O^T += V^T P^T with V^T fragments from the
   // transposed LDS read (rows 16c + tr_row and +8).
   auto softmax_pv = [&](int j, const f32x16 (&s)[BC / 32]) {
-    const uint8_t* Vs = smem + (j & 1) * Cfg::STAGE_B + TILE_B;
+    const uint8_t* Vs = smem + (j % NS) * Cfg::STAGE_B + TILE_B;
     const float neg_m = -m_ref;
     vec8 pf[BC / 16];
     float ls = 0.f;
@@ -269,16 +271,18 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   // done outside it and the loop resumes. Keeping the conditional rescale out of the loop body
   // keeps the accumulator in one set of registers (a join inside the loop made the compiler copy
   // all of it on every tile).
-  issue(0);
+  for (int t = 0; t < NS - 1 && t < n_kv; ++t) issue(t);
   int j = 0;
   f32x16 s[BC / 32];
   float m_new = 0.f;
   while (j < n_kv) {
     bool grew = false;
     for (; j < n_kv; ++j) {
-      wait_vmcnt<0>();  // this wave's loads of tile j have landed
-      barrier_lds();    // ... and everyone's; stage (j + 1) & 1 is no longer being read
-      if (j + 1 < n_kv) issue(j + 1);
+      // this wave's loads of tile j have landed (tiles j+1 .. j+NS-2 may still be in flight)
+      if (j + NS - 2 < n_kv) wait_vmcnt<(NS - 2) * Cfg::LPI>();
+      else wait_vmcnt<0>();
+      barrier_lds();  // ... and everyone's; stage (j - 1) % NS is no longer being read
+      if (j + NS - 1 < n_kv) issue(j + NS - 1);
       if (!(wave_active && j * BC < wave_kv_end)) continue;
       const float mx = scores(j, s);
       m_new = fmaxf(m_ref, mx);
@@ -501,7 +505,7 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel_f32(FwdArgsF32 a) {
 // ---------------------------------------------------------------------------------------------
 // Dispatch.
 
-template <typename TR, int D, int BR, int BC>
+template <typename TR, int D, int BR, int BC, int NS>
 hipError_t launch16(const FwdReq& r, hipStream_t st) {
   FwdArgs a;
   a.q = (const uint16_t*)r.q;
@@ -520,11 +524,11 @@ hipError_t launch16(const FwdReq& r, hipStream_t st) {
   // buffer offsets are 32-bit: heads of 2 GiB or more take the 64-bit address path
   const bool big = (size_t)r.N * D * 2 >= ((size_t)1 << 31);
   if (r.causal) {
-    if (big) hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, true, false>), grid, block, 0, st, a);
+    if (big) hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, true, false>), grid, block, 0, st, a);
   } else {
-    if (big) hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, false, false>), grid, block, 0, st, a);
+    if (big) hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, false, false>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -552,10 +556,12 @@ hipError_t launch32(const FwdReq& r, hipStream_t st) {
 
 template <typename TR, int D>
 hipError_t launch16_tile(const FwdReq& r, hipStream_t st) {
-  if (r.Br == 128 && r.Bc == 64) return launch16<TR, D, 128, 64>(r, st);
-  if (r.Br == 128 && r.Bc == 128) return launch16<TR, D, 128, 128>(r, st);
-  if (r.Br == 64 && r.Bc == 64) return launch16<TR, D, 64, 64>(r, st);
-  if (r.Br == 64 && r.Bc == 128) return launch16<TR, D, 64, 128>(r, st);
+  if (r.Br == 128 && r.Bc == 64) return launch16<TR, D, 128, 64, 2>(r, st);
+  if (r.Br == 128 && r.Bc == 128) return launch16<TR, D, 128, 128, 2>(r, st);
+  if (r.Br == 64 && r.Bc == 64) return launch16<TR, D, 64, 64, 2>(r, st);
+  if (r.Br == 64 && r.Bc == 128) return launch16<TR, D, 64, 128, 2>(r, st);
+  if (r.Br == 256 && r.Bc == 64) return launch16<TR, D, 256, 64, 2>(r, st);
+  if (r.Br == 256 && r.Bc == 128) return launch16<TR, D, 256, 128, 2>(r, st);
   return hipErrorInvalidValue;
 }
 
@@ -564,7 +570,8 @@ hipError_t launch16_tile(const FwdReq& r, hipStream_t st) {
 bool fwd_tile_supported(int dtype, int d, int Br, int Bc) {
   if (d != 64 && d != 128) return false;
   if (dtype == FATTN_F32) return Bc == 32 && (Br == 64 || Br == 128);
-  if (dtype == FATTN_F16 || dtype == FATTN_BF16) return (Br == 64 || Br == 128) && (Bc == 64 || Bc == 128);
+  if (dtype == FATTN_F16 || dtype == FATTN_BF16)
+    return (Br == 64 || Br == 128 || Br == 256) && (Bc == 64 || Bc == 128);
   return false;
 }
 
@@ -577,8 +584,10 @@ bool fwd_default_tile(int dtype, int d, int causal, int* Br, int* Bc) {
     return true;
   }
   if (dtype == FATTN_F16 || dtype == FATTN_BF16) {
-    *Br = 128;
-    *Bc = 64;
+    // measured on MI355X: at d = 128, eight waves sharing 128-key tiles (128 KiB of LDS, one
+    // work-group per CU) beat four waves on 64-key tiles by 4-10%; at d = 64 the smaller tile wins
+    *Br = d == 128 ? 256 : 128;
+    *Bc = d == 128 ? 128 : 64;
     return true;
   }
   return false;

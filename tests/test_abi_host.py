@@ -65,6 +65,7 @@ def fwd(**kw):
     (dict(d=96), -3), (dict(d=32), -3), (dict(d=256), -3), (dict(d=0), -3),
     (dict(dtype=3), -4), (dict(dtype=-1), -4),
     (dict(Br=96, Bc=64), -5), (dict(Br=128, Bc=32), -5), (dict(Br=64, Bc=0), -5),
+    (dict(Br=512, Bc=64), -5), (dict(Br=256, Bc=32), -5), (dict(Br=256, Bc=256), -5),
     (dict(dtype=fa.FATTN_F32, Br=128, Bc=64), -5),
     (dict(q=MIS), -6), (dict(o=MIS), -6), (dict(lse=MIS), -6),
     (dict(scale=float("nan")), -7), (dict(scale=float("inf")), -7), (dict(scale=-math.inf), -7),

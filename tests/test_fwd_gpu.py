@@ -66,7 +66,7 @@ def test_forward_small_shapes(dtype, d, N, causal):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("tile", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("tile", [(64, 64), (64, 128), (128, 64), (128, 128), (256, 64), (256, 128)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_forward_every_tile_shape(dtype, tile, causal):
     B, H, N, d = 2, 2, 333, 128
@@ -198,7 +198,7 @@ def _workload_heads(ident, causal, Br=0, Bc=0):
     return inp, o, lse
 
 
-@pytest.mark.parametrize("tile", [(0, 0), (64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("tile", [(0, 0), (64, 64), (64, 128), (128, 64), (128, 128), (256, 64), (256, 128)])
 def test_workload3_bf16_causal_tiles(tile):
     log(f"workload 3 tile {tile}")
     _workload_heads(3, True, *tile)
