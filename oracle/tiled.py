@@ -16,6 +16,9 @@ Algorithm, in the pages' order and notation:
   section: m_new = max(m, m_b), l_new = exp(m - m_new) l + exp(m_b - m_new) l_b and
   u_new = exp(m - m_new) u + exp(m_b - m_new) u_b.
 * After the last block, O = u / l (page 2, rescale-identity section; page 3, same section).
+* ``forward_slice_kouter`` runs the same blocks in the other loop order (key/value blocks outer,
+  query blocks inner, page 2's FA-1 to FA-2 section), keeping every query block's state between
+  visits; it exists to pin the ablation of that order.
 * Causal masking happens inside the block: a key index above the query index is dropped, and a
   block lying wholly above the diagonal is not visited at all (page 2, backward section and
   tips). Blocks at the end of the sequence may be short (page 2, tips).
@@ -95,6 +98,46 @@ def forward_slice(q, k, v, scale, Br, Bc, causal=False, trace=None):
         o[i0:i1] = u / l[:, None]
         lse[i0:i1] = m + np.log(l)
     return o, lse, visited
+
+
+def forward_slice_kouter(q, k, v, scale, Br, Bc, causal=False, trace=None):
+    """The same tiled forward in the K-outer order (page 2, FA-1 to FA-2 section).
+
+    The key/value block j is the outer loop and the query blocks the inner one, so every visit
+    (i, j) reloads query block i and its running state (m, l, u), which the Q-outer order keeps
+    on chip. The state of every query block lives in ``states`` between visits (HBM, on a
+    device). Each row still merges its key blocks in increasing j with the same rule, so the
+    result equals ``forward_slice`` exactly. Returns (O, LSE, visits); ``trace`` receives
+    (i_block, j_block, m, l, u) after every merge, in visiting order.
+    """
+    q, k, v = (np.asarray(t, np.float64) for t in (q, k, v))
+    N, d = q.shape
+    Nk = k.shape[0]
+    states = {}
+    visits = 0
+    for j0 in range(0, Nk, Bc):
+        j1 = min(Nk, j0 + Bc)
+        for i0 in range(0, N, Br):
+            i1 = min(N, i0 + Br)
+            if causal and j0 > i1 - 1:
+                continue  # this key block lies wholly above the diagonal of query block i
+            m, l, u = states.get(i0, (np.full(i1 - i0, NEG_INF), np.zeros(i1 - i0),
+                                      np.zeros((i1 - i0, v.shape[1]))))
+            s = (q[i0:i1] @ k[j0:j1].T) * scale
+            if causal:
+                rows = np.arange(i0, i1)[:, None]
+                cols = np.arange(j0, j1)[None, :]
+                s = np.where(cols > rows, NEG_INF, s)
+            states[i0] = merge(m, l, u, *block_stats(s, v[j0:j1]))
+            visits += 1
+            if trace is not None:
+                trace.append((i0 // Br, j0 // Bc) + tuple(x.copy() for x in states[i0]))
+    o = np.empty((N, v.shape[1]))
+    lse = np.empty(N)
+    for i0, (m, l, u) in states.items():
+        o[i0:i0 + len(l)] = u / l[:, None]
+        lse[i0:i0 + len(l)] = m + np.log(l)
+    return o, lse, visits
 
 
 def forward(q, k, v, scale, Br, Bc, causal=False):

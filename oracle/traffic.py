@@ -16,6 +16,16 @@ It does not print the numbers, so the counts here are this model's reading of it
 ``tiled_bytes_with_rereads`` adds what the pages leave out: every query block of Br rows reads
 all of K and V again unless a cache holds them, so the tiled traffic without any cache reuse is
 2 N d (N / Br) elements for K and V instead of 2 N d.
+
+``loop_order_bytes`` counts, for either loop order (page 2, FA-1 to FA-2 section), the bytes a
+kernel that keeps nothing in a cache between tiles must move, visit by visit:
+
+* Q-outer: each query block is read once and its O (elem_bytes) and LSE (4 B) written once;
+  every visited (i, j) pair reads key/value block j (2 rows x d elements per key).
+* K-outer: each key/value block is read once; every visited (i, j) pair reads query block i, and
+  the block's running state (u in float32 plus m and l, (d + 2) x 4 B per row) is read back
+  unless it is the block's first visit and written out unless it is its last, when O and LSE
+  are written instead.
 """
 from __future__ import annotations
 
@@ -58,3 +68,38 @@ def print_traffic_table(seq_lengths=(128, 256, 512, 1024, 2048, 4096), d: int = 
         print(f"{r['N']:>6} {r['naive_nn_elements']:>16} {r['naive_bytes'] / 2**20:>10.3f} "
               f"{r['flash_nn_elements']:>10} {r['flash_bytes'] / 2**20:>10.3f}")
     return rows
+
+
+def loop_order_bytes(N: int, d: int, Br: int, Bc: int, order: str, causal: bool = False,
+                     elem_bytes: int = 2) -> int:
+    """HBM bytes of one head for ``order`` in {"q_outer", "k_outer"}, with no cache reuse."""
+    if order not in ("q_outer", "k_outer"):
+        raise ValueError(order)
+    q_blocks = [(i0, min(N, i0 + Br)) for i0 in range(0, N, Br)]
+    k_blocks = [(j0, min(N, j0 + Bc)) for j0 in range(0, N, Bc)]
+    total = 0
+    if order == "q_outer":
+        for i0, i1 in q_blocks:
+            rows = i1 - i0
+            total += rows * d * elem_bytes                      # Q block, once
+            for j0, j1 in k_blocks:
+                if causal and j0 > i1 - 1:
+                    break
+                total += 2 * (j1 - j0) * d * elem_bytes         # K and V block, every visit
+            total += rows * d * elem_bytes + rows * 4           # O and LSE, once
+        return total
+    for j0, j1 in k_blocks:
+        total += 2 * (j1 - j0) * d * elem_bytes                 # K and V block, once
+    state = (d + 2) * 4                                         # u, m, l per row, float32
+    for i0, i1 in q_blocks:
+        rows = i1 - i0
+        visits = [j0 for j0, _ in k_blocks if not (causal and j0 > i1 - 1)]
+        for n, _ in enumerate(visits):
+            total += rows * d * elem_bytes                      # Q block, every visit
+            if n > 0:
+                total += rows * state                           # state read back
+            if n < len(visits) - 1:
+                total += rows * state                           # state written out
+            else:
+                total += rows * d * elem_bytes + rows * 4       # O and LSE at the last visit
+    return total

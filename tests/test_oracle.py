@@ -435,3 +435,59 @@ def test_inputs_are_seeded_and_independent_per_tensor():
     c = fi.make_inputs((1, 2, 16, 8), "bf16", 4)
     assert not np.array_equal(a.q, c.q)
     assert b.do is not None and b.do.shape == (1, 2, 16, 8)
+
+
+# --------------------------------------------------------------------------------------------
+# K-outer loop order (page 2, FA-1 to FA-2 section): the ablation's model
+
+
+@pytest.mark.parametrize("N,Br,Bc,causal", [(1, 1, 1, False), (37, 5, 3, True), (100, 16, 64, False),
+                                            (129, 64, 16, True), (200, 32, 32, True), (64, 128, 64, False)])
+def test_kouter_equals_qouter_bitwise_and_the_definition(N, Br, Bc, causal):
+    r = _rng(71, N, Br, Bc, int(causal))
+    q, k, v = (r.standard_normal((N, 8)) for _ in range(3))
+    o1, l1, vis1 = tiled.forward_slice(q, k, v, 0.4, Br, Bc, causal)
+    trace = []
+    o2, l2, vis2 = tiled.forward_slice_kouter(q, k, v, 0.4, Br, Bc, causal, trace=trace)
+    # every row merges the same blocks in the same order: identical float64 results
+    np.testing.assert_array_equal(o2, o1)
+    np.testing.assert_array_equal(l2, l1)
+    assert vis1 == vis2
+    if causal:
+        assert vis2 == tiled.causal_blocks_visited(N, Br, Bc)
+    else:
+        assert vis2 == math.ceil(N / Br) * math.ceil(N / Bc)
+    # the visiting order is key-block major
+    order = [(jb, ib) for ib, jb, *_ in trace]
+    assert order == sorted(order)
+    o_ref, l_ref = att.forward_slice(q, k, v, 0.4, causal)
+    np.testing.assert_allclose(o2, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2, l_ref, rtol=0, atol=1e-12)
+
+
+def test_kouter_worked_example_fifty_thirds():
+    g, q, k, v = _p3_case()
+    o, lse, visits = tiled.forward_slice_kouter(q, k, v, 1.0, Br=1, Bc=1)
+    assert visits == 2
+    assert o[0, 0] == pytest.approx(_expr(g["output"]), abs=1e-13)
+    assert lse[0] == pytest.approx(math.log(3.0), abs=1e-15)
+
+
+def test_loop_order_bytes_closed_forms():
+    N, d, s = 4096, 128, 2
+    for Br, Bc in ((128, 64), (256, 128), (64, 64)):
+        # Q-outer, no cache: Q + O once, LSE once, K and V once per query block
+        q_outer = traffic.loop_order_bytes(N, d, Br, Bc, "q_outer")
+        assert q_outer == 2 * N * d * s + 4 * N + 2 * N * d * s * (N // Br)
+        assert q_outer == traffic.tiled_bytes_with_rereads(N, d, Br, s)
+        # K-outer: K, V once; Q once per key block; state (d + 2) floats per row read and written
+        # on every visit but the first / last; O and LSE once
+        nb = N // Bc
+        k_outer = traffic.loop_order_bytes(N, d, Br, Bc, "k_outer")
+        assert k_outer == 2 * N * d * s + nb * N * d * s + 2 * (nb - 1) * N * (d + 2) * 4 + N * d * s + 4 * N
+    # the K-outer order moves more bytes whenever there is more than one key block
+    assert traffic.loop_order_bytes(N, d, 128, 64, "k_outer") > 4 * traffic.loop_order_bytes(N, d, 128, 64, "q_outer")
+    # causal: the visit counts fall to the lower triangle in both orders
+    qc = traffic.loop_order_bytes(N, d, 128, 128, "q_outer", causal=True)
+    nb = N // 128
+    assert qc == 2 * N * d * s + 4 * N + 2 * 128 * d * s * (nb * (nb + 1) // 2)
