@@ -189,6 +189,14 @@ def main(argv=None):
 
     ms_step = T(step)
 
+    # Ablation: the same forward in the K-outer loop order (one launch per key block, query tile
+    # and running state reloaded from HBM on every visit).
+    ws_ko = torch.empty(fa.fattn_fwd_kouter_workspace_size(B, H, N, d, fa.FATTN_BF16), dtype=torch.uint8,
+                        device="cuda")
+    o_ko, l_ko = torch.empty_like(q), torch.empty_like(lse)
+    ms_kouter = T(lambda: fa.forward_kouter(q, k, v, causal=True, out=o_ko, lse=l_ko, workspace=ws_ko))
+    del ws_ko, o_ko, l_ko
+
     # Prefill-shaped forward (B=4).
     ms_fwd3 = T(lambda: fa.forward(q3, k3, v3, causal=True, out=o3, lse=l3))
     del q3, k3, v3, o3, l3
@@ -296,6 +304,21 @@ def main(argv=None):
         "kernel_ms": {k_: round(t, 4) for k_, t in ms.items()},
         "roofline": roof,
     }
+    ko_launches = (N + 127) // 128
+    ko = {"workload": "B=2 H=16 N=4096 d=128 causal, K-outer order (FA-1), 256 x 128 tiles",
+          "ms": round(ms_kouter, 4), "tflops": round(tf(f_fwd, ms_kouter), 1),
+          "time_vs_q_outer": round(ms_kouter / ms["fwd"], 2), "launches": ko_launches}
+    if tr_all:
+        recs = [r for (kn, _), r in tr_all.items() if kn.startswith("ko_kernel<Bf16, 128, 256, 128, true>")]
+        if recs:
+            ko["hbm_bytes_per_call"] = {"fetch": round(recs[0]["fetch_bytes"] * ko_launches),
+                                        "write": round(recs[0]["write_bytes"] * ko_launches),
+                                        "source": "profiles/traffic.json (per-launch mean x launches)"}
+        fw = [r for (kn, g), r in tr_all.items() if kn.startswith(kernels["fwd"][3]) and g == kernels["fwd"][2]]
+        if fw:
+            ko["q_outer_hbm_bytes_per_call"] = {"fetch": round(fw[0]["fetch_bytes"]),
+                                                "write": round(fw[0]["write_bytes"])}
+    result["ablation_kouter"] = ko
     if decode:
         result["decode"] = decode
     if not a.no_cpu_baseline:

@@ -131,6 +131,20 @@ int fattn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, co
                  int dtype, void* stream);
 
 /*
+ * The forward in the K-outer loop order, an ablation (page 2, section on going from
+ * FlashAttention-1 to FlashAttention-2: with key/value blocks outer, each query block and its
+ * running statistics have to be reloaded for every key block). Same inputs, outputs and result
+ * as fattn_fwd (f16/bf16 only); one kernel launch per key/value block, each work-group reading
+ * its query tile and its float32 running state (u [B,H,N,d], m and l [B,H,N]) from `workspace`
+ * and writing it back, or O and LSE at its last block. `workspace` holds at least
+ * fattn_fwd_kouter_workspace_size() bytes; contents on entry are ignored, on exit unspecified.
+ */
+size_t fattn_fwd_kouter_workspace_size(int B, int H, int N, int d, int dtype);
+int fattn_fwd_kouter(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int N, int d, float scale, int causal, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Split-KV forward: Nq query rows per head against an Nk-long key/value cache, computed as
  * per-range partial results merged afterwards. This is the decode shape (page "mianstack q-0277",
  * backward section, names the key/value cache): the keys of each row are cut into num_splits

@@ -7,9 +7,10 @@ stream; there is no CPU or PyTorch fallback, and a missing library raises.
 Low-level names mirror the C entry points (``fattn_fwd``, ``fattn_fwd_tiled``, ``fattn_bwd``,
 ``fattn_bwd_workspace_size``, ``fattn_bwd_preprocess``, ``fattn_bwd_dkdv``, ``fattn_bwd_dv``,
 ``fattn_bwd_dk``, ``fattn_bwd_dq``, ``fattn_fwd_splitkv``, ``fattn_fwd_splitkv_workspace_size``,
-``fattn_splitkv_num_splits``, ``fattn_fwd_partial``, ``fattn_combine``,
+``fattn_splitkv_num_splits``, ``fattn_fwd_partial``, ``fattn_combine``, ``fattn_fwd_kouter``,
+``fattn_fwd_kouter_workspace_size``,
 ``fattn_strerror``, ``fattn_version``) and take raw device addresses. ``forward``, ``backward``,
-``backward_stages``, ``forward_splitkv``, ``forward_partial`` and ``combine`` wrap them for
+``backward_stages``, ``forward_splitkv``, ``forward_partial``, ``combine`` and ``forward_kouter`` wrap them for
 contiguous torch tensors.
 """
 from __future__ import annotations
@@ -25,6 +26,7 @@ __all__ = [
     "fattn_version", "forward", "backward", "backward_stages", "dtype_code",
     "fattn_fwd_splitkv", "fattn_fwd_splitkv_workspace_size", "fattn_splitkv_num_splits",
     "fattn_fwd_partial", "fattn_combine", "forward_splitkv", "forward_partial", "combine",
+    "fattn_fwd_kouter", "fattn_fwd_kouter_workspace_size", "forward_kouter",
 ]
 
 FATTN_F32, FATTN_F16, FATTN_BF16 = 0, 1, 2
@@ -79,6 +81,10 @@ def lib():
     L.fattn_fwd_partial.restype = i
     L.fattn_combine.argtypes = [vp, vp, i, vp, vp, i, i, i, i, i, vp]
     L.fattn_combine.restype = i
+    L.fattn_fwd_kouter_workspace_size.argtypes = [i, i, i, i, i]
+    L.fattn_fwd_kouter_workspace_size.restype = sz
+    L.fattn_fwd_kouter.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
+    L.fattn_fwd_kouter.restype = i
     L.fattn_strerror.argtypes = [i]
     L.fattn_strerror.restype = ctypes.c_char_p
     L.fattn_version.argtypes = []
@@ -150,6 +156,16 @@ def fattn_fwd_partial(q, k, v, o_parts, lse_parts, B, H, Nq, Nk, d, scale, causa
 
 def fattn_combine(o_parts, lse_parts, num_splits, o, lse, B, H, Nq, d, dtype, stream=None) -> int:
     return lib().fattn_combine(o_parts, lse_parts, num_splits, o, lse, B, H, Nq, d, dtype, stream)
+
+
+def fattn_fwd_kouter_workspace_size(B, H, N, d, dtype) -> int:
+    return lib().fattn_fwd_kouter_workspace_size(B, H, N, d, dtype)
+
+
+def fattn_fwd_kouter(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, workspace, workspace_bytes,
+                     stream=None) -> int:
+    return lib().fattn_fwd_kouter(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, workspace,
+                                  workspace_bytes, stream)
 
 
 def fattn_strerror(status: int) -> str:
@@ -354,4 +370,29 @@ def combine(o_parts, lse_parts, dtype=None, out=None, lse=None, stream=None):
                        B, H, Nq, d, dtype_code(out), _stream(stream))
     if st != 0:
         raise FattnError(st, "fattn_combine")
+    return out, lse
+
+
+def forward_kouter(q, k, v, causal=False, scale=None, out=None, lse=None, workspace=None, stream=None):
+    """O, LSE by the K-outer loop order (the ablation); same contract as ``forward``."""
+    import torch
+    _check(q, "q")
+    _check(k, "k", q)
+    _check(v, "v", q)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = dtype_code(q)
+    need = fattn_fwd_kouter_workspace_size(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = fattn_fwd_kouter(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          B, H, N, d, float(scale), int(bool(causal)), code, workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != 0:
+        raise FattnError(st, "fattn_fwd_kouter")
     return out, lse

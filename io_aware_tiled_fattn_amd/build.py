@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libfattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["fattn_api.cpp", "fattn_fwd.hip", "fattn_bwd.hip", "fattn_splitkv.hip"]
+SOURCES = ["fattn_api.cpp", "fattn_fwd.hip", "fattn_bwd.hip", "fattn_splitkv.hip", "fattn_kouter.hip"]
 
 ARCH = "gfx950"
 COMMON = [

@@ -230,6 +230,31 @@ int fattn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, co
   return launch_status(fattn::launch_bwd(r, (hipStream_t)stream, 2));
 }
 
+size_t fattn_fwd_kouter_workspace_size(int B, int H, int N, int d, int dtype) {
+  if (check_common(B, H, N, d, dtype) != FATTN_OK || dtype == FATTN_F32) return 0;
+  return fattn::kouter_workspace_bytes(B, H, N, d);
+}
+
+int fattn_fwd_kouter(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int N, int d, float scale, int causal, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FATTN_ERR_NULL;
+  int st = check_common(B, H, N, d, dtype);
+  if (st != FATTN_OK) return st;
+  if (dtype == FATTN_F32) return FATTN_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FATTN_ERR_CAUSAL;
+  if (!std::isfinite(scale)) return FATTN_ERR_SCALE;
+  if (!workspace || workspace_bytes < fattn::kouter_workspace_bytes(B, H, N, d)) return FATTN_ERR_WORKSPACE;
+  const void* all[6] = {q, k, v, o, lse, workspace};
+  for (const void* p : all)
+    if (!aligned16(p)) return FATTN_ERR_ALIGN;
+  for (int i = 3; i < 6; ++i)
+    for (int j = 0; j < 6; ++j)
+      if (i != j && all[i] == all[j]) return FATTN_ERR_ALIAS;
+  fattn::KoReq r{q, k, v, o, lse, B, H, N, d, scale, causal, dtype, (float*)workspace};
+  return launch_status(fattn::launch_kouter(r, (hipStream_t)stream));
+}
+
 int fattn_splitkv_num_splits(int B, int H, int Nq, int Nk, int d) {
   if (check_split_shape(B, H, Nq, Nk, d, 1) != FATTN_OK) return 0;
   return auto_splits(B, H, Nq, Nk);

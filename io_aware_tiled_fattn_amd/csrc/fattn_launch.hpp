@@ -76,4 +76,20 @@ int splitkv_split_len(int Nk, int num_splits);
 hipError_t launch_splitkv_partial(const SplitReq& r, hipStream_t stream);
 hipError_t launch_combine(const CombineReq& r, hipStream_t stream);
 
+// K-outer (FA-1 order) forward, an ablation: one launch per key/value block.
+struct KoReq {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, N, d;
+  float scale;
+  int causal;
+  int dtype;
+  float* workspace;  // running state: u [B*H*N*d], m [B*H*N], l [B*H*N], float32
+};
+size_t kouter_workspace_bytes(int B, int H, int N, int d);
+hipError_t launch_kouter(const KoReq& r, hipStream_t stream);
+
 }  // namespace fattn

@@ -22,7 +22,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-KERNEL_SOURCES = ("fattn_device.hpp", "fattn_fwd.hip", "fattn_bwd.hip", "fattn_splitkv.hip")
+KERNEL_SOURCES = ("fattn_device.hpp", "fattn_fwd.hip", "fattn_bwd.hip", "fattn_splitkv.hip",
+                  "fattn_kouter.hip")
 DECODE_KERNELS = ("splitkv_kernel", "combine_kernel")
 COPY_BYTES = 256 * 2**20  # the calibration copy reads and writes this many bytes each
 
@@ -49,7 +50,7 @@ def source_hash() -> str:
 def short_name(kernel: str) -> str:
     k = kernel.replace("fattn::(anonymous namespace)::", "").replace("fattn::", "")
     k = k.replace("(unsigned short const*, unsigned short const*, float*, long long)", "")
-    for args in ("FwdArgs", "BwdArgs", "SplitArgs", "CombineArgs"):
+    for args in ("FwdArgs", "BwdArgs", "SplitArgs", "CombineArgs", "KoArgs"):
         k = k.replace(f"((anonymous namespace)::{args})", "")
     return k.replace("void ", "").strip()
 
@@ -131,9 +132,11 @@ def write_summaries(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
     tr, fc, wc = traffic(run_dir)
     cmd_note = "Commands (from the repository root, on the GPU box; RUN is an output folder):\n\n"
     titles = {
-        workload: (f"bench.py step workload ({workload}) and the B=4 forward",
+        workload: (f"bench.py step workload ({workload}), the B=4 forward and the K-outer ablation",
                    "The forward kernel's calls mix the B=2 (step) and B=4 (prefill) workloads; "
-                   "bench.py times each live with HIP events."),
+                   "bench.py times each live with HIP events. `ko_kernel` is the K-outer ablation on "
+                   "the step's forward shape, one launch per 128-key block (32 per call), so its "
+                   "per-launch figures are 1/32 of a call."),
         DECODE_WORKLOAD: ("bench.py split-KV decode workloads (B=8 H=32 Nk=16384 d=128 bf16, "
                           "Nq = 1 and Nq = 16, one shared cache)",
                           "The partial kernel's calls mix Nq = 1 and Nq = 16 (same grid); the "

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(L):
             "fattn_strerror", "fattn_version", "fattn_bwd_preprocess", "fattn_bwd_dkdv",
             "fattn_bwd_dv", "fattn_bwd_dk", "fattn_bwd_dq", "fattn_fwd_splitkv",
             "fattn_fwd_splitkv_workspace_size", "fattn_splitkv_num_splits", "fattn_fwd_partial",
-            "fattn_combine"} <= set(names)
+            "fattn_combine", "fattn_fwd_kouter", "fattn_fwd_kouter_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
         assert getattr(fa, n) is not None
@@ -210,3 +210,27 @@ def test_splitkv_rejects_bad_arguments(L, kw, status):
 ])
 def test_partial_and_combine_reject_bad_arguments(L, call, status):
     assert call() == status
+
+
+# --------------------------------------------------------------------------------------------
+# K-outer ablation
+
+
+def test_kouter_workspace_size(L):
+    n = fa.fattn_fwd_kouter_workspace_size(2, 16, 4096, 128, fa.FATTN_BF16)
+    assert n == _r256(2 * 16 * 4096 * 130 * 4)
+    assert fa.fattn_fwd_kouter_workspace_size(2, 16, 4096, 128, fa.FATTN_F32) == 0
+    assert fa.fattn_fwd_kouter_workspace_size(2, 16, 4096, 96, fa.FATTN_BF16) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(lse=None), -1), (dict(dtype=fa.FATTN_F32), -4), (dict(d=96), -3),
+    (dict(N=0), -2), (dict(causal=2), -12), (dict(scale=float("nan")), -7), (dict(ws=None), -8),
+    (dict(wsb=16), -8), (dict(ws=MIS), -6), (dict(o=P[1]), -11), (dict(ws=P[0]), -11),
+])
+def test_kouter_rejects_bad_arguments(L, kw, status):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=16, d=64, scale=0.1, causal=0,
+             dtype=fa.FATTN_BF16, ws=P[5], wsb=1 << 20)
+    a.update(kw)
+    assert fa.fattn_fwd_kouter(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                               a["scale"], a["causal"], a["dtype"], a["ws"], a["wsb"]) == status
