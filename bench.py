@@ -197,6 +197,11 @@ def main(argv=None):
     ms_kouter = T(lambda: fa.forward_kouter(q, k, v, causal=True, out=o_ko, lse=l_ko, workspace=ws_ko))
     del ws_ko, o_ko, l_ko
 
+    # Dropout (p = 0.1) on the same step: forward and backward with the Philox keep mask.
+    p_drop, seed = 0.1, 1234
+    ms_drop_fwd = T(lambda: fa.forward(q, k, v, causal=True, out=o, lse=lse, p_drop=p_drop, seed=seed))
+    ms_drop_bwd = T(lambda: fa.backward(q, k, v, o, do, lse, causal=True, workspace=ws, p_drop=p_drop, seed=seed))
+
     # Prefill-shaped forward (B=4).
     ms_fwd3 = T(lambda: fa.forward(q3, k3, v3, causal=True, out=o3, lse=l3))
     del q3, k3, v3, o3, l3
@@ -319,6 +324,12 @@ def main(argv=None):
             ko["q_outer_hbm_bytes_per_call"] = {"fetch": round(fw[0]["fetch_bytes"]),
                                                 "write": round(fw[0]["write_bytes"])}
     result["ablation_kouter"] = ko
+    result["dropout"] = {"workload": "B=2 H=16 N=4096 d=128 causal, p = 0.1 (Philox4x32-10 keep mask)",
+                         "fwd_ms": round(ms_drop_fwd, 4), "bwd_ms": round(ms_drop_bwd, 4),
+                         "fwd_tflops": round(tf(f_fwd, ms_drop_fwd), 1),
+                         "bwd_tflops": round(tf(2.5 * f_fwd, ms_drop_bwd), 1),
+                         "fwd_time_vs_plain": round(ms_drop_fwd / ms["fwd"], 2),
+                         "bwd_time_vs_plain": round(ms_drop_bwd / ms["bwd"], 2)}
     if decode:
         result["decode"] = decode
     if not a.no_cpu_baseline:

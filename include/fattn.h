@@ -58,7 +58,8 @@ typedef enum {
   FATTN_ERR_UNSUPPORTED = -9, /* a valid request this build does not implement */
   FATTN_ERR_LAUNCH = -10,     /* the HIP runtime rejected a kernel launch */
   FATTN_ERR_ALIAS = -11,      /* an output pointer equals an input pointer */
-  FATTN_ERR_CAUSAL = -12      /* causal not 0 or 1 */
+  FATTN_ERR_CAUSAL = -12,     /* causal not 0 or 1 */
+  FATTN_ERR_DROPOUT = -13     /* dropout probability not in [0, 1) */
 } fattn_status;
 
 /*
@@ -84,6 +85,20 @@ int fattn_fwd_tiled(const void* q, const void* k, const void* v, void* o, float*
                     int Br, int Bc, void* stream);
 
 /*
+ * Forward with dropout on the attention probabilities (page "mianstack q-0277", section on
+ * whether the result changes, names dropout as a training-time source of difference; the pages
+ * fix no convention, so this one is stated here). With P = softmax(S) and keep mask M:
+ *     O = ((P * M) / (1 - p_drop)) V,   LSE = the undropped statistic (as fattn_fwd writes it).
+ * M(b, h, i, j) = 1 iff x >= floor(p_drop * 2^32), where x is word j % 4 of Philox4x32-10 (Salmon
+ * et al., SC 2011) at counter (j / 4, i, b*H + h, 0) with key (seed mod 2^32, seed / 2^32). The
+ * same (seed, p_drop) reproduces the same mask in fattn_bwd_dropout. p_drop in [0, 1), else
+ * FATTN_ERR_DROPOUT; p_drop = 0 is fattn_fwd. f16/bf16 only; uses the default tile shape.
+ */
+int fattn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int N, int d, float scale, int causal, int dtype,
+                      float p_drop, unsigned long long seed, void* stream);
+
+/*
  * Bytes of device workspace fattn_bwd needs: the float32 row vector D = rowsum(dO * O) [B,H,N],
  * rounded up to 256 bytes. Returns 0 for arguments that fattn_bwd would reject on shape, head
  * dim or dtype grounds.
@@ -102,6 +117,18 @@ int fattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
               const float* lse, void* dq, void* dk, void* dv,
               int B, int H, int N, int d, float scale, int causal, int dtype,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of fattn_fwd_dropout (same p_drop and seed, hence the same mask M): with
+ * Pd = P * M / (1 - p_drop), dV = Pd^T dO, dP = (dO V^T) * M / (1 - p_drop), D = rowsum(dO * O),
+ * dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q. Same buffers and checks as fattn_bwd;
+ * p_drop = 0 is fattn_bwd.
+ */
+int fattn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                      const float* lse, void* dq, void* dk, void* dv,
+                      int B, int H, int N, int d, float scale, int causal, int dtype,
+                      float p_drop, unsigned long long seed,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The three stages of fattn_bwd, in the order fattn_bwd enqueues them, for callers that want to

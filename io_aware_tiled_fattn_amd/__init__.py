@@ -8,7 +8,7 @@ Low-level names mirror the C entry points (``fattn_fwd``, ``fattn_fwd_tiled``, `
 ``fattn_bwd_workspace_size``, ``fattn_bwd_preprocess``, ``fattn_bwd_dkdv``, ``fattn_bwd_dv``,
 ``fattn_bwd_dk``, ``fattn_bwd_dq``, ``fattn_fwd_splitkv``, ``fattn_fwd_splitkv_workspace_size``,
 ``fattn_splitkv_num_splits``, ``fattn_fwd_partial``, ``fattn_combine``, ``fattn_fwd_kouter``,
-``fattn_fwd_kouter_workspace_size``,
+``fattn_fwd_kouter_workspace_size``, ``fattn_fwd_dropout``, ``fattn_bwd_dropout``,
 ``fattn_strerror``, ``fattn_version``) and take raw device addresses. ``forward``, ``backward``,
 ``backward_stages``, ``forward_splitkv``, ``forward_partial``, ``combine`` and ``forward_kouter`` wrap them for
 contiguous torch tensors.
@@ -27,6 +27,7 @@ __all__ = [
     "fattn_fwd_splitkv", "fattn_fwd_splitkv_workspace_size", "fattn_splitkv_num_splits",
     "fattn_fwd_partial", "fattn_combine", "forward_splitkv", "forward_partial", "combine",
     "fattn_fwd_kouter", "fattn_fwd_kouter_workspace_size", "forward_kouter",
+    "fattn_fwd_dropout", "fattn_bwd_dropout",
 ]
 
 FATTN_F32, FATTN_F16, FATTN_BF16 = 0, 1, 2
@@ -85,6 +86,11 @@ def lib():
     L.fattn_fwd_kouter_workspace_size.restype = sz
     L.fattn_fwd_kouter.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
     L.fattn_fwd_kouter.restype = i
+    u64 = ctypes.c_ulonglong
+    L.fattn_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, f, u64, vp]
+    L.fattn_fwd_dropout.restype = i
+    L.fattn_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, f, u64, vp, sz, vp]
+    L.fattn_bwd_dropout.restype = i
     L.fattn_strerror.argtypes = [i]
     L.fattn_strerror.restype = ctypes.c_char_p
     L.fattn_version.argtypes = []
@@ -168,6 +174,16 @@ def fattn_fwd_kouter(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, workspac
                                   workspace_bytes, stream)
 
 
+def fattn_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, p_drop, seed, stream=None) -> int:
+    return lib().fattn_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, p_drop, seed, stream)
+
+
+def fattn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, p_drop, seed,
+                      workspace, workspace_bytes, stream=None) -> int:
+    return lib().fattn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype,
+                                   p_drop, seed, workspace, workspace_bytes, stream)
+
+
 def fattn_strerror(status: int) -> str:
     return lib().fattn_strerror(status).decode()
 
@@ -202,10 +218,13 @@ def _stream(stream):
     return s.cuda_stream
 
 
-def forward(q, k, v, causal=False, scale=None, Br=0, Bc=0, out=None, lse=None, stream=None):
+def forward(q, k, v, causal=False, scale=None, Br=0, Bc=0, out=None, lse=None, stream=None,
+            p_drop=0.0, seed=0):
     """O, LSE for contiguous [B, H, N, d] device tensors (float32, float16 or bfloat16).
 
     ``out`` and ``lse`` may be given to write into existing tensors (no allocation then).
+    ``p_drop`` > 0 applies dropout to P with the keep mask of ``seed`` (fattn_fwd_dropout;
+    16-bit types, default tile shape).
     """
     import torch
     _check(q, "q")
@@ -219,6 +238,15 @@ def forward(q, k, v, causal=False, scale=None, Br=0, Bc=0, out=None, lse=None, s
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check(out, "out", q)
+    if p_drop:
+        if Br or Bc:
+            raise ValueError("dropout runs with the default tile shape")
+        st = fattn_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               B, H, N, d, float(scale), int(bool(causal)), dtype_code(q), float(p_drop),
+                               int(seed), _stream(stream))
+        if st != 0:
+            raise FattnError(st, "fattn_fwd_dropout")
+        return out, lse
     st = fattn_fwd_tiled(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                          B, H, N, d, float(scale), int(bool(causal)), dtype_code(q), int(Br), int(Bc),
                          _stream(stream))
@@ -227,8 +255,10 @@ def forward(q, k, v, causal=False, scale=None, Br=0, Bc=0, out=None, lse=None, s
     return out, lse
 
 
-def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, stream=None):
-    """dQ, dK, dV for contiguous [B, H, N, d] float16/bfloat16 device tensors."""
+def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, stream=None, p_drop=0.0,
+             seed=0):
+    """dQ, dK, dV for contiguous [B, H, N, d] float16/bfloat16 device tensors (with dropout of
+    ``p_drop`` and ``seed`` when p_drop > 0: the same mask as the forward)."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _check(t, n, q if n != "q" else None)
@@ -240,6 +270,15 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, stre
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if p_drop:
+        st = fattn_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                               lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                               B, H, N, d, float(scale), int(bool(causal)), code, float(p_drop), int(seed),
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               _stream(stream))
+        if st != 0:
+            raise FattnError(st, "fattn_bwd_dropout")
+        return dq, dk, dv
     st = fattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                    B, H, N, d, float(scale), int(bool(causal)), code,

@@ -30,6 +30,19 @@ int check_common(int B, int H, int N, int d, int dtype) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? FATTN_OK : FATTN_ERR_LAUNCH; }
 
+// Keep threshold floor(p 2^32) and 1 / (1 - p) of a drop probability p in (0, 1).
+fattn::DropParams drop_params(float p, unsigned long long seed) {
+  fattn::DropParams d;
+  d.seed_lo = (uint32_t)(seed & 0xffffffffull);
+  d.seed_hi = (uint32_t)(seed >> 32);
+  const double t = std::floor((double)p * 4294967296.0);
+  d.thr = t >= 4294967295.0 ? 0xffffffffu : (uint32_t)t;
+  d.inv_keep = (float)(1.0 / (1.0 - (double)p));
+  return d;
+}
+
+bool drop_ok(float p) { return std::isfinite(p) && p >= 0.f && p < 1.f; }
+
 constexpr int kMaxSplits = 1024;
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -88,6 +101,7 @@ const char* fattn_strerror(int status) {
     case FATTN_ERR_LAUNCH: return "kernel launch failed";
     case FATTN_ERR_ALIAS: return "an output aliases an input";
     case FATTN_ERR_CAUSAL: return "causal must be 0 or 1";
+    case FATTN_ERR_DROPOUT: return "dropout probability not in [0, 1)";
     default: return "unknown status";
   }
 }
@@ -118,6 +132,30 @@ int fattn_fwd_tiled(const void* q, const void* k, const void* v, void* o, float*
 int fattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int N, int d, float scale, int causal, int dtype, void* stream) {
   return fattn_fwd_tiled(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, 0, 0, stream);
+}
+
+int fattn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int N, int d, float scale, int causal, int dtype,
+                      float p_drop, unsigned long long seed, void* stream) {
+  if (!drop_ok(p_drop)) return FATTN_ERR_DROPOUT;
+  if (dtype == FATTN_F32) return FATTN_ERR_DTYPE;
+  if (p_drop == 0.f) return fattn_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream);
+  if (!q || !k || !v || !o || !lse) return FATTN_ERR_NULL;
+  int st = check_common(B, H, N, d, dtype);
+  if (st != FATTN_OK) return st;
+  if (causal != 0 && causal != 1) return FATTN_ERR_CAUSAL;
+  if (!std::isfinite(scale)) return FATTN_ERR_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FATTN_ERR_ALIGN;
+  if (o == q || o == k || o == v || (const void*)lse == q || (const void*)lse == k ||
+      (const void*)lse == v || (void*)lse == o)
+    return FATTN_ERR_ALIAS;
+  int Br = 0, Bc = 0;
+  if (!fattn::fwd_default_tile(dtype, d, causal, &Br, &Bc)) return FATTN_ERR_TILE;
+  fattn::FwdReq r{q, k, v, o, lse, B, H, N, d, scale, causal, dtype, Br, Bc};
+  r.dropout = true;
+  r.drop = drop_params(p_drop, seed);
+  return launch_status(fattn::launch_fwd(r, (hipStream_t)stream));
 }
 
 size_t fattn_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
@@ -154,6 +192,44 @@ int fattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
   for (const void* s : ins)
     if (s == workspace) return FATTN_ERR_ALIAS;
   fattn::BwdReq r{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, (float*)workspace};
+  return launch_status(fattn::launch_bwd(r, (hipStream_t)stream));
+}
+
+int fattn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                      const float* lse, void* dq, void* dk, void* dv,
+                      int B, int H, int N, int d, float scale, int causal, int dtype,
+                      float p_drop, unsigned long long seed,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!drop_ok(p_drop)) return FATTN_ERR_DROPOUT;
+  if (p_drop == 0.f)
+    return fattn_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, workspace,
+                     workspace_bytes, stream);
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FATTN_ERR_NULL;
+  int st = check_common(B, H, N, d, dtype);
+  if (st != FATTN_OK) return st;
+  if (dtype == FATTN_F32) return FATTN_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FATTN_ERR_CAUSAL;
+  if (!std::isfinite(scale)) return FATTN_ERR_SCALE;
+  const void* ins[6] = {q, k, v, o, dO, lse};
+  void* outs[3] = {dq, dk, dv};
+  for (const void* p : ins)
+    if (!aligned16(p)) return FATTN_ERR_ALIGN;
+  for (void* p : outs)
+    if (!aligned16(p)) return FATTN_ERR_ALIGN;
+  for (void* p : outs)
+    for (const void* s2 : ins)
+      if (p == s2) return FATTN_ERR_ALIAS;
+  if (dq == dk || dq == dv || dk == dv) return FATTN_ERR_ALIAS;
+  const size_t need = fattn::bwd_workspace_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < need) return FATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FATTN_ERR_ALIGN;
+  for (void* p : outs)
+    if (p == workspace) return FATTN_ERR_ALIAS;
+  for (const void* s2 : ins)
+    if (s2 == workspace) return FATTN_ERR_ALIAS;
+  fattn::BwdReq r{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, (float*)workspace};
+  r.dropout = true;
+  r.drop = drop_params(p_drop, seed);
   return launch_status(fattn::launch_bwd(r, (hipStream_t)stream));
 }
 

@@ -46,6 +46,7 @@ struct BwdArgs {
   int bh_total; // B * H
   float c;      // scale * log2(e) (signed)
   float scale;  // signed softmax scale
+  DropParams drop;  // dropout on P (DROP instances only)
 };
 
 template <typename TR>
@@ -148,7 +149,9 @@ struct DkdvCfg {
 // dK += dS^T Q: 3 GEMMs). The two passes recompute S, one GEMM more than a fused pass, but each
 // holds half the accumulators: both fit in 256 registers, so two waves share every SIMD and their
 // MFMA and VALU work overlaps (a fused pass needs ~300 registers and runs one wave per SIMD).
-template <typename TR, int D, bool CAUSAL, bool BIG, int MODE>
+// DROP: dropout on P with mask M (Pd = P M / (1 - p)): the dV pass accumulates Pd^T dO, the dK
+// pass uses dS = P (dO V^T M / (1 - p) - D); D = rowsum(dO O) is unchanged.
+template <typename TR, int D, bool CAUSAL, bool BIG, int MODE, bool DROP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(BwdArgs a) {
   static_assert(MODE == 1 || MODE == 2, "dV pass or dK pass");
   constexpr bool DO_DV = MODE == 1, DO_DK = MODE == 2;
@@ -323,11 +326,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         for (int j = 0; j < 4; ++j) {
           f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
           if (DO_DK) d4 = *(const f32x4*)(dvs + qb * 32 + 8 * j + 4 * h);
+          // keep bits of this lane's key for queries q_base + qb*32 + 8j + 4h + r, r = 0..3
+          uint32_t kbits = 0xFu;
+          if (DROP)
+            kbits = quad_keep_bits((uint32_t)key >> 2, (uint32_t)(q_base + qb * 32 + 8 * j + 4 * h), (uint32_t)bh,
+                                   a.drop, lane);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int e = 4 * j + r;
             p[e] = __builtin_amdgcn_exp2f(s[e]);
-            ds[e] = p[e] * (dp[e] - d4[r]);
+            if (DROP) {
+              const bool kept = (kbits >> r) & 1u;
+              if (DO_DK) ds[e] = p[e] * ((kept ? dp[e] * a.drop.inv_keep : 0.f) - d4[r]);
+              if (DO_DV) p[e] = kept ? p[e] * a.drop.inv_keep : 0.f;
+            } else {
+              ds[e] = p[e] * (dp[e] - d4[r]);
+            }
           }
         }
         vec8 pp[2], dsp[2];
@@ -408,7 +422,8 @@ struct DqCfg {
   static_assert(BK * CPR % NT == 0, "tile split");
 };
 
-template <typename TR, int D, bool CAUSAL, bool BIG>
+// DROP: dS = P (dO V^T M / (1 - p) - D).
+template <typename TR, int D, bool CAUSAL, bool BIG, bool DROP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BwdArgs a) {
   using Cfg = DqCfg<D>;
   using vec8 = typename TR::vec8;
@@ -535,12 +550,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       vec8 dsp[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
+        u32x4 wd[2];
+        if (DROP) {
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+            wd[g] = philox4x32_10((uint32_t)(k0 / 4 + 8 * kb + 2 * (2 * half + g) + h), (uint32_t)qrow,
+                                  (uint32_t)bh, 0u, a.drop.seed_lo, a.drop.seed_hi);
+        }
         u32x4 packed;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const int e = 8 * half + 2 * e2;
-          const float ds0 = __builtin_amdgcn_exp2f(s[e]) * (dp[e] - dval);
-          const float ds1 = __builtin_amdgcn_exp2f(s[e + 1]) * (dp[e + 1] - dval);
+          float dp0 = dp[e], dp1 = dp[e + 1];
+          if (DROP) {
+            dp0 = wd[e2 >> 1][2 * (e2 & 1)] >= a.drop.thr ? dp0 * a.drop.inv_keep : 0.f;
+            dp1 = wd[e2 >> 1][2 * (e2 & 1) + 1] >= a.drop.thr ? dp1 * a.drop.inv_keep : 0.f;
+          }
+          const float ds0 = __builtin_amdgcn_exp2f(s[e]) * (dp0 - dval);
+          const float ds1 = __builtin_amdgcn_exp2f(s[e + 1]) * (dp1 - dval);
           packed[e2] = TR::pack2(ds0, ds1);
         }
         dsp[half] = bitcast<vec8>(packed);
@@ -575,7 +602,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 
 // ---------------------------------------------------------------------------------------------
 
-template <typename TR, int D>
+template <typename TR, int D, bool DROP>
 hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
   BwdArgs a;
   a.q = (const uint16_t*)r.q;
@@ -591,6 +618,7 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
   a.N = r.N;
   a.c = r.scale * kLog2e;
   a.scale = r.scale;
+  a.drop = r.drop;
   const long long BH = (long long)r.B * r.H;
   const long long rows = BH * r.N;
 
@@ -610,11 +638,11 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
     auto go = [&](auto kern) { hipLaunchKernelGGL(kern, g1, dim3(256), 0, st, a); };
     const bool dv_pass = stage != 4, dk_pass = stage != 3;
     if (r.causal) {
-      if (dv_pass) big ? go(bwd_dkdv_kernel<TR, D, true, true, 1>) : go(bwd_dkdv_kernel<TR, D, true, false, 1>);
-      if (dk_pass) big ? go(bwd_dkdv_kernel<TR, D, true, true, 2>) : go(bwd_dkdv_kernel<TR, D, true, false, 2>);
+      if (dv_pass) big ? go(bwd_dkdv_kernel<TR, D, true, true, 1, DROP>) : go(bwd_dkdv_kernel<TR, D, true, false, 1, DROP>);
+      if (dk_pass) big ? go(bwd_dkdv_kernel<TR, D, true, true, 2, DROP>) : go(bwd_dkdv_kernel<TR, D, true, false, 2, DROP>);
     } else {
-      if (dv_pass) big ? go(bwd_dkdv_kernel<TR, D, false, true, 1>) : go(bwd_dkdv_kernel<TR, D, false, false, 1>);
-      if (dk_pass) big ? go(bwd_dkdv_kernel<TR, D, false, true, 2>) : go(bwd_dkdv_kernel<TR, D, false, false, 2>);
+      if (dv_pass) big ? go(bwd_dkdv_kernel<TR, D, false, true, 1, DROP>) : go(bwd_dkdv_kernel<TR, D, false, false, 1, DROP>);
+      if (dk_pass) big ? go(bwd_dkdv_kernel<TR, D, false, true, 2, DROP>) : go(bwd_dkdv_kernel<TR, D, false, false, 2, DROP>);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -623,11 +651,11 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
     a.ntiles = (r.N + DqCfg<D>::BQ - 1) / DqCfg<D>::BQ;
     dim3 g2((unsigned)(BH * a.ntiles));
     if (r.causal) {
-      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, true>), g2, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, false>), g2, dim3(256), 0, st, a);
+      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, true, DROP>), g2, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, false, DROP>), g2, dim3(256), 0, st, a);
     } else {
-      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, true>), g2, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, false>), g2, dim3(256), 0, st, a);
+      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, true, DROP>), g2, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, false, DROP>), g2, dim3(256), 0, st, a);
     }
     e = hipGetLastError();
   }
@@ -642,12 +670,17 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   return (dvec + 255) & ~(size_t)255;
 }
 
-hipError_t launch_bwd(const BwdReq& r, hipStream_t st, int stage) {
+template <bool DROP>
+hipError_t launch_bwd_t(const BwdReq& r, hipStream_t st, int stage) {
   if (r.dtype == FATTN_BF16)
-    return r.d == 64 ? launch_all<Bf16, 64>(r, st, stage) : launch_all<Bf16, 128>(r, st, stage);
+    return r.d == 64 ? launch_all<Bf16, 64, DROP>(r, st, stage) : launch_all<Bf16, 128, DROP>(r, st, stage);
   if (r.dtype == FATTN_F16)
-    return r.d == 64 ? launch_all<F16, 64>(r, st, stage) : launch_all<F16, 128>(r, st, stage);
+    return r.d == 64 ? launch_all<F16, 64, DROP>(r, st, stage) : launch_all<F16, 128, DROP>(r, st, stage);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd(const BwdReq& r, hipStream_t st, int stage) {
+  return r.dropout ? launch_bwd_t<true>(r, st, stage) : launch_bwd_t<false>(r, st, stage);
 }
 
 }  // namespace fattn

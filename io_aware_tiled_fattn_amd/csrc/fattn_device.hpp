@@ -136,6 +136,52 @@ __device__ inline int swz_dual(int row) {
   return D == 128 ? 4 * (row & 3) + ((row >> 2) & 3) : 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
 }
 
+// ---- dropout keep mask ---------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011): ten rounds of
+//   (hi0, lo0) = M0 * c0, (hi1, lo1) = M1 * c2, c = (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0),
+// the key bumped by the Weyl constants between rounds.
+__device__ inline u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                      uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// The keep decision of (head bh, query i, key j) is word j % 4 of Philox4x32-10 at counter
+// (j / 4, i, bh, 0) under the 64-bit seed, compared with floor(p 2^32).
+struct DropParams {
+  uint32_t seed_lo, seed_hi;
+  uint32_t thr;      // floor(p * 2^32)
+  float inv_keep;    // 1 / (1 - p)
+};
+
+// Keep bits of 4 consecutive keys of one key group (held by the 4 lanes of a quad, one key per
+// lane, key % 4 = lane % 4) for the 4 consecutive queries q4 .. q4 + 3: every lane draws the
+// generator for one query (q4 + lane % 4), turns its 4 words into a 4-bit mask (bit r = key r),
+// and the quad exchanges the masks over DPP. Bit t of the result is the keep bit of this lane's
+// key for query q4 + t. Every lane of the quad must be active.
+template <int T>
+__device__ inline uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, T | (T << 2) | (T << 4) | (T << 6), 0xF, 0xF, false);
+}
+__device__ inline uint32_t quad_keep_bits(uint32_t kgroup, uint32_t q4, uint32_t bh, const DropParams& dp, int lane) {
+  const u32x4 w = philox4x32_10(kgroup, q4 + (uint32_t)(lane & 3), bh, 0u, dp.seed_lo, dp.seed_hi);
+  const uint32_t m = (w[0] >= dp.thr ? 1u : 0u) | (w[1] >= dp.thr ? 2u : 0u) | (w[2] >= dp.thr ? 4u : 0u) |
+                     (w[3] >= dp.thr ? 8u : 0u);
+  const uint32_t r = (uint32_t)(lane & 3);
+  return ((quad_bcast<0>(m) >> r) & 1u) | (((quad_bcast<1>(m) >> r) & 1u) << 1) |
+         (((quad_bcast<2>(m) >> r) & 1u) << 2) | (((quad_bcast<3>(m) >> r) & 1u) << 3);
+}
+
 // Block index remap so that consecutive logical blocks share an XCD: hardware dispatches block
 // ids round-robin over the 8 XCDs, so physical id x runs on XCD x % 8. When the grid is a
 // multiple of 8 the logical order visits, per XCD, one contiguous range of work.

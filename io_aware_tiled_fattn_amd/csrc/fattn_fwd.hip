@@ -53,6 +53,7 @@ struct FwdArgs {
   float c;             // |scale| * log2(e), > 0
   uint32_t neg_mask;   // 0x80008000 flips the sign of two packed 16-bit Q elements (scale < 0)
   uint32_t keep_mask;  // 0 zeroes Q (scale == 0: every logit is 0), else all ones
+  DropParams drop;     // dropout on P (used by the DROP instances only)
 };
 
 // Block id -> (head, query tile). Hardware deals block ids round-robin over the 8 XCDs, so
@@ -96,7 +97,9 @@ struct FwdCfg {
 
 // BIG: the head's K/V exceed the 32-bit range of buffer offsets, so tiles are fetched with
 // per-lane 64-bit global addresses instead.
-template <typename TR, int D, int BR, int BC, int NS, bool CAUSAL, bool BIG>
+// DROP: dropout on P. The exp-sum l keeps every key (LSE is the undropped statistic); a dropped
+// key's probability is zeroed before the PV product, and O is scaled by 1 / (1 - p) at the end.
+template <typename TR, int D, int BR, int BC, int NS, bool CAUSAL, bool BIG, bool DROP>
 __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   using Cfg = FwdCfg<D, BR, BC, NS>;
   using vec8 = typename TR::vec8;
@@ -241,12 +244,25 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
+        // keys of elements 8 half + 4 g + r (g = 0, 1): key group (j BC + 32 kb + 8 (2 half + g)
+        // + 4 h) / 4, word r
+        u32x4 wd[2];
+        if (DROP) {
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+            wd[g] = philox4x32_10((uint32_t)((j * BC) / 4 + 8 * kb + 2 * (2 * half + g) + h), (uint32_t)qrow,
+                                  (uint32_t)bh, 0u, a.drop.seed_lo, a.drop.seed_hi);
+        }
         u32x4 packed;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * e2], a.c, neg_m));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * e2 + 1], a.c, neg_m));
+          float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * e2], a.c, neg_m));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * e2 + 1], a.c, neg_m));
           ls += p0 + p1;
+          if (DROP) {
+            p0 = wd[e2 >> 1][2 * (e2 & 1)] >= a.drop.thr ? p0 : 0.f;
+            p1 = wd[e2 >> 1][2 * (e2 & 1) + 1] >= a.drop.thr ? p1 : 0.f;
+          }
           packed[e2] = TR::pack2(p0, p1);
         }
         pf[2 * kb + half] = bitcast<vec8>(packed);
@@ -309,7 +325,7 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   if (!wave_active) return;
   const float l_tot = sum_halves(l_part);
   if (qrow >= N) return;
-  const float inv = 1.0f / l_tot;
+  const float inv = (DROP ? a.drop.inv_keep : 1.0f) / l_tot;
   uint16_t* Orow = a.o + head + (size_t)qrow * D;
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
@@ -505,7 +521,7 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel_f32(FwdArgsF32 a) {
 // ---------------------------------------------------------------------------------------------
 // Dispatch.
 
-template <typename TR, int D, int BR, int BC, int NS>
+template <typename TR, int D, int BR, int BC, int NS, bool DROP = false>
 hipError_t launch16(const FwdReq& r, hipStream_t st) {
   FwdArgs a;
   a.q = (const uint16_t*)r.q;
@@ -519,16 +535,17 @@ hipError_t launch16(const FwdReq& r, hipStream_t st) {
   a.c = r.scale == 0.f ? 1.f : fabsf(r.scale) * kLog2e;
   a.neg_mask = r.scale < 0.f ? 0x80008000u : 0u;
   a.keep_mask = r.scale == 0.f ? 0u : 0xffffffffu;
+  a.drop = r.drop;
   const long long nblk = (long long)r.B * r.H * a.n_qtiles;
   const dim3 grid((unsigned)nblk), block(BR / 32 * 64);
   // buffer offsets are 32-bit: heads of 2 GiB or more take the 64-bit address path
   const bool big = (size_t)r.N * D * 2 >= ((size_t)1 << 31);
   if (r.causal) {
-    if (big) hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, true, false>), grid, block, 0, st, a);
+    if (big) hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, true, true, DROP>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, true, false, DROP>), grid, block, 0, st, a);
   } else {
-    if (big) hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, false, false>), grid, block, 0, st, a);
+    if (big) hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, false, true, DROP>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, false, false, DROP>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -556,6 +573,11 @@ hipError_t launch32(const FwdReq& r, hipStream_t st) {
 
 template <typename TR, int D>
 hipError_t launch16_tile(const FwdReq& r, hipStream_t st) {
+  if (r.dropout) {  // dropout instances exist for the default tiles only
+    if (D == 128 && r.Br == 256 && r.Bc == 128) return launch16<TR, D, 256, 128, 2, true>(r, st);
+    if (D == 64 && r.Br == 128 && r.Bc == 64) return launch16<TR, D, 128, 64, 2, true>(r, st);
+    return hipErrorInvalidValue;
+  }
   if (r.Br == 128 && r.Bc == 64) return launch16<TR, D, 128, 64, 2>(r, st);
   if (r.Br == 128 && r.Bc == 128) return launch16<TR, D, 128, 128, 2>(r, st);
   if (r.Br == 64 && r.Bc == 64) return launch16<TR, D, 64, 64, 2>(r, st);

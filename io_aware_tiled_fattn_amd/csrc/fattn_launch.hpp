@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "fattn_device.hpp"
+
 namespace fattn {
 
 struct FwdReq {
@@ -17,6 +19,8 @@ struct FwdReq {
   int causal;
   int dtype;  // fattn_dtype
   int Br, Bc; // resolved tile shape (never 0 here)
+  bool dropout = false;  // dropout on P with `drop` (default tiles, 16-bit types only)
+  DropParams drop = {0u, 0u, 0u, 1.0f};
 };
 
 struct BwdReq {
@@ -34,6 +38,8 @@ struct BwdReq {
   int causal;
   int dtype;
   float* dvec;  // workspace: D = rowsum(dO * O), float32 [B, H, N]
+  bool dropout = false;
+  DropParams drop = {0u, 0u, 0u, 1.0f};
 };
 
 // Default forward tile for (dtype, d, causal): returns false if none exists.

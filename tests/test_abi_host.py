@@ -36,7 +36,8 @@ def test_every_declared_symbol_is_exported(L):
             "fattn_strerror", "fattn_version", "fattn_bwd_preprocess", "fattn_bwd_dkdv",
             "fattn_bwd_dv", "fattn_bwd_dk", "fattn_bwd_dq", "fattn_fwd_splitkv",
             "fattn_fwd_splitkv_workspace_size", "fattn_splitkv_num_splits", "fattn_fwd_partial",
-            "fattn_combine", "fattn_fwd_kouter", "fattn_fwd_kouter_workspace_size"} <= set(names)
+            "fattn_combine", "fattn_fwd_kouter", "fattn_fwd_kouter_workspace_size",
+            "fattn_fwd_dropout", "fattn_bwd_dropout"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
         assert getattr(fa, n) is not None
@@ -44,7 +45,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_strerror(L):
     assert fa.fattn_version() >= 100
-    for code in range(0, -13, -1):
+    for code in range(0, -14, -1):
         s = fa.fattn_strerror(code)
         assert s and s != "unknown status", code
     assert fa.fattn_strerror(12345) == "unknown status"
@@ -234,3 +235,30 @@ def test_kouter_rejects_bad_arguments(L, kw, status):
     a.update(kw)
     assert fa.fattn_fwd_kouter(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
                                a["scale"], a["causal"], a["dtype"], a["ws"], a["wsb"]) == status
+
+
+# --------------------------------------------------------------------------------------------
+# Dropout
+
+
+@pytest.mark.parametrize("p,dtype,status", [
+    (1.0, 2, -13), (-0.1, 2, -13), (float("nan"), 2, -13), (1.5, 1, -13), (0.1, 0, -4), (0.1, 7, -4),
+])
+def test_fwd_dropout_rejects_bad_arguments(L, p, dtype, status):
+    assert fa.fattn_fwd_dropout(P[0], P[1], P[2], P[3], P[4], 1, 1, 16, 64, 0.1, 0, dtype, p, 1) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=1.0), -13), (dict(p=-1e-9), -13), (dict(dq=None), -1), (dict(ws=None), -8), (dict(dtype=0), -4),
+    (dict(dk=P[0]), -11), (dict(d=96), -3), (dict(causal=4), -12),
+])
+def test_bwd_dropout_rejects_bad_arguments(L, kw, status):
+    a = dict(p=0.2, dq=P[6], dk=P[7], ws=P[9], dtype=2, d=64, causal=0)
+    a.update(kw)
+    assert fa.fattn_bwd_dropout(P[0], P[1], P[2], P[3], P[4], P[5], a["dq"], a["dk"], P[8], 1, 1, 16, a["d"], 0.1,
+                                a["causal"], a["dtype"], a["p"], 7, a["ws"], 1 << 20) == status
+
+
+def test_dropout_seed_is_64_bit(L):
+    # a seed above 2^32 passes the host checks (rejected here only for the fake NULL output)
+    assert fa.fattn_fwd_dropout(P[0], P[1], P[2], None, P[4], 1, 1, 16, 64, 0.1, 0, 2, 0.3, 2**63 + 5) == -1
