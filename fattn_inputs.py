@@ -186,6 +186,16 @@ def decode_workload_inputs(ident: int, with_q: bool = True, with_kv: bool = True
                               with_q=with_q, with_kv=with_kv)
 
 
+def block_mask(B, H, nb, density, seed, diagonal=True):
+    """Seeded 0/1 block mask [B, H, nb, nb] (uint8): each block kept with probability ``density``;
+    with ``diagonal`` the diagonal blocks are always kept, so every query row has a key."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 77]))
+    m = (rng.random((B, H, nb, nb)) < density).astype(np.uint8)
+    if diagonal:
+        m[..., np.arange(nb), np.arange(nb)] = 1
+    return m
+
+
 def unshifted_partner(inp: Inputs, scale: float) -> Inputs:
     """For variant 1, the tensors whose logits are exactly 500 lower than ``inp``'s.
 

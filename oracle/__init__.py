@@ -9,6 +9,7 @@ Modules:
   attention  the definition (stable row-max softmax) forward and the analytic backward, fp64
   tiled      a float64 model of the tiled forward with the online (m, l, u) merge, used only to
              pin the algorithm the pages describe (never the device's ground truth)
+  blocksparse exact attention restricted to allowed 128 x 128 (query, key) blocks
   dropout    attention with dropout on P and its Philox4x32-10 keep mask
   splitkv    split-KV partials (O_s, LSE_s) over key ranges and their merge by the page-3 rule
   traffic    the analytic naive-versus-tiled HBM traffic model
@@ -18,4 +19,4 @@ Every function is pinned by tests that do not retype it: the pages' worked examp
 (tests/golden), closed forms, invariances, library cross-checks (scipy) and finite-difference
 gradients.
 """
-from . import attention, dropout, metrics, splitkv, tiled, traffic  # noqa: F401
+from . import attention, blocksparse, dropout, metrics, splitkv, tiled, traffic  # noqa: F401
