@@ -197,6 +197,21 @@ def main(argv=None):
     ms_kouter = T(lambda: fa.forward_kouter(q, k, v, causal=True, out=o_ko, lse=l_ko, workspace=ws_ko))
     del ws_ko, o_ko, l_ko
 
+    # Block-sparse forward on the step's shape: 128 x 128 blocks kept with probability 1/4, plus
+    # the diagonal, under the causal mask.
+    import numpy as np
+    nbk = N // 128
+    bmask_np = fi.block_mask(B, H, nbk, 0.25, 5)
+    bmask = torch.from_numpy(bmask_np).cuda()
+    ms_bs = T(lambda: fa.forward_blocksparse(q, k, v, bmask, causal=True, out=o, lse=lse))
+    # allowed (query, key) pairs: full blocks below the diagonal, half (with the diagonal) on it
+    tri = np.tril(np.ones((nbk, nbk), bool), -1)
+    pairs_bs = float((bmask_np.astype(bool) & tri).sum() * 128 * 128
+                     + np.diagonal(bmask_np, axis1=2, axis2=3).astype(bool).sum() * 128 * 129 // 2)
+    f_bs = 4.0 * d * pairs_bs
+    density = pairs_bs / (B * H * N * (N + 1) / 2)
+    fa.forward(q, k, v, causal=True, out=o, lse=lse)  # leave the step's O and LSE in place
+
     # Dropout (p = 0.1) on the same step: forward and backward with the Philox keep mask.
     p_drop, seed = 0.1, 1234
     ms_drop_fwd = T(lambda: fa.forward(q, k, v, causal=True, out=o, lse=lse, p_drop=p_drop, seed=seed))
@@ -324,6 +339,11 @@ def main(argv=None):
             ko["q_outer_hbm_bytes_per_call"] = {"fetch": round(fw[0]["fetch_bytes"]),
                                                 "write": round(fw[0]["write_bytes"])}
     result["ablation_kouter"] = ko
+    result["blocksparse"] = {"workload": "B=2 H=16 N=4096 d=128 causal, 128x128 blocks kept with p = 1/4 "
+                                         "plus the diagonal",
+                             "ms": round(ms_bs, 4), "allowed_fraction_of_causal_pairs": round(density, 4),
+                             "tflops_on_allowed_pairs": round(tf(f_bs, ms_bs), 1),
+                             "time_vs_dense": round(ms_bs / ms["fwd"], 3)}
     result["dropout"] = {"workload": "B=2 H=16 N=4096 d=128 causal, p = 0.1 (Philox4x32-10 keep mask)",
                          "fwd_ms": round(ms_drop_fwd, 4), "bwd_ms": round(ms_drop_bwd, 4),
                          "fwd_tflops": round(tf(f_fwd, ms_drop_fwd), 1),

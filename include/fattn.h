@@ -99,6 +99,20 @@ int fattn_fwd_dropout(const void* q, const void* k, const void* v, void* o, floa
                       float p_drop, unsigned long long seed, void* stream);
 
 /*
+ * Block-sparse forward: exact attention restricted to the allowed 128 x 128 (query, key) blocks
+ * (page "FlashAttention为什么更快更省显存", section on computing in blocks, mentions the
+ * block-sparse approximate variant without defining it; this is the reading stated here).
+ * block_mask: device uint8 [B, H, nb, nb], nb = ceil(N / 128); block (r, c) covers queries
+ * [128 r, 128 r + 128) and keys [128 c, 128 c + 128); nonzero = computed. Scores outside allowed
+ * blocks (and above the diagonal when causal) are -inf; a row with no allowed key gets O = 0 and
+ * LSE = -inf. Key tiles whose blocks are zero for a whole work-group are neither read nor
+ * computed. f16/bf16 only; default tile shape; same other conventions as fattn_fwd.
+ */
+int fattn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int N, int d, float scale, int causal, int dtype,
+                          const unsigned char* block_mask, void* stream);
+
+/*
  * Bytes of device workspace fattn_bwd needs: the float32 row vector D = rowsum(dO * O) [B,H,N],
  * rounded up to 256 bytes. Returns 0 for arguments that fattn_bwd would reject on shape, head
  * dim or dtype grounds.

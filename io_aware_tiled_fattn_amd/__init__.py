@@ -9,6 +9,7 @@ Low-level names mirror the C entry points (``fattn_fwd``, ``fattn_fwd_tiled``, `
 ``fattn_bwd_dk``, ``fattn_bwd_dq``, ``fattn_fwd_splitkv``, ``fattn_fwd_splitkv_workspace_size``,
 ``fattn_splitkv_num_splits``, ``fattn_fwd_partial``, ``fattn_combine``, ``fattn_fwd_kouter``,
 ``fattn_fwd_kouter_workspace_size``, ``fattn_fwd_dropout``, ``fattn_bwd_dropout``,
+``fattn_fwd_blocksparse``,
 ``fattn_strerror``, ``fattn_version``) and take raw device addresses. ``forward``, ``backward``,
 ``backward_stages``, ``forward_splitkv``, ``forward_partial``, ``combine`` and ``forward_kouter`` wrap them for
 contiguous torch tensors.
@@ -27,7 +28,7 @@ __all__ = [
     "fattn_fwd_splitkv", "fattn_fwd_splitkv_workspace_size", "fattn_splitkv_num_splits",
     "fattn_fwd_partial", "fattn_combine", "forward_splitkv", "forward_partial", "combine",
     "fattn_fwd_kouter", "fattn_fwd_kouter_workspace_size", "forward_kouter",
-    "fattn_fwd_dropout", "fattn_bwd_dropout",
+    "fattn_fwd_dropout", "fattn_bwd_dropout", "fattn_fwd_blocksparse", "forward_blocksparse",
 ]
 
 FATTN_F32, FATTN_F16, FATTN_BF16 = 0, 1, 2
@@ -91,6 +92,8 @@ def lib():
     L.fattn_fwd_dropout.restype = i
     L.fattn_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, f, u64, vp, sz, vp]
     L.fattn_bwd_dropout.restype = i
+    L.fattn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, vp]
+    L.fattn_fwd_blocksparse.restype = i
     L.fattn_strerror.argtypes = [i]
     L.fattn_strerror.restype = ctypes.c_char_p
     L.fattn_version.argtypes = []
@@ -182,6 +185,10 @@ def fattn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal
                       workspace, workspace_bytes, stream=None) -> int:
     return lib().fattn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype,
                                    p_drop, seed, workspace, workspace_bytes, stream)
+
+
+def fattn_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, block_mask, stream=None) -> int:
+    return lib().fattn_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, block_mask, stream)
 
 
 def fattn_strerror(status: int) -> str:
@@ -434,4 +441,28 @@ def forward_kouter(q, k, v, causal=False, scale=None, out=None, lse=None, worksp
                           workspace.numel() * workspace.element_size(), _stream(stream))
     if st != 0:
         raise FattnError(st, "fattn_fwd_kouter")
+    return out, lse
+
+
+def forward_blocksparse(q, k, v, block_mask, causal=False, scale=None, out=None, lse=None, stream=None):
+    """O, LSE of block-sparse attention; ``block_mask`` is a uint8 device tensor [B, H, nb, nb]
+    over 128 x 128 (query, key) blocks, nb = ceil(N / 128)."""
+    import torch
+    _check(q, "q")
+    _check(k, "k", q)
+    _check(v, "v", q)
+    B, H, N, d = q.shape
+    nb = (N + 127) // 128
+    _check_dev(block_mask, "block_mask", (B, H, nb, nb), torch.uint8)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = fattn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               B, H, N, d, float(scale), int(bool(causal)), dtype_code(q),
+                               block_mask.data_ptr(), _stream(stream))
+    if st != 0:
+        raise FattnError(st, "fattn_fwd_blocksparse")
     return out, lse

@@ -134,6 +134,30 @@ int fattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   return fattn_fwd_tiled(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, 0, 0, stream);
 }
 
+int fattn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int N, int d, float scale, int causal, int dtype,
+                          const unsigned char* block_mask, void* stream) {
+  if (!q || !k || !v || !o || !lse || !block_mask) return FATTN_ERR_NULL;
+  if (dtype == FATTN_F32) return FATTN_ERR_DTYPE;
+  int st = check_common(B, H, N, d, dtype);
+  if (st != FATTN_OK) return st;
+  if (causal != 0 && causal != 1) return FATTN_ERR_CAUSAL;
+  if (!std::isfinite(scale)) return FATTN_ERR_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FATTN_ERR_ALIGN;
+  const void* outs[2] = {o, lse};
+  const void* ins[4] = {q, k, v, block_mask};
+  for (const void* p : outs)
+    for (const void* i2 : ins)
+      if (p == i2) return FATTN_ERR_ALIAS;
+  if (o == (void*)lse) return FATTN_ERR_ALIAS;
+  int Br = 0, Bc = 0;
+  if (!fattn::fwd_default_tile(dtype, d, causal, &Br, &Bc)) return FATTN_ERR_TILE;
+  fattn::FwdReq r{q, k, v, o, lse, B, H, N, d, scale, causal, dtype, Br, Bc};
+  r.bmask = block_mask;
+  return launch_status(fattn::launch_fwd(r, (hipStream_t)stream));
+}
+
 int fattn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int H, int N, int d, float scale, int causal, int dtype,
                       float p_drop, unsigned long long seed, void* stream) {

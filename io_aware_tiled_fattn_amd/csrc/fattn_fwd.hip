@@ -54,6 +54,8 @@ struct FwdArgs {
   uint32_t neg_mask;   // 0x80008000 flips the sign of two packed 16-bit Q elements (scale < 0)
   uint32_t keep_mask;  // 0 zeroes Q (scale == 0: every logit is 0), else all ones
   DropParams drop;     // dropout on P (used by the DROP instances only)
+  const uint8_t* bmask;  // block mask [B*H][nb][nb] over 128 x 128 (query, key) blocks (SPARSE)
+  int nb;                // ceil(N / 128)
 };
 
 // Block id -> (head, query tile). Hardware deals block ids round-robin over the 8 XCDs, so
@@ -99,7 +101,10 @@ struct FwdCfg {
 // per-lane 64-bit global addresses instead.
 // DROP: dropout on P. The exp-sum l keeps every key (LSE is the undropped statistic); a dropped
 // key's probability is zeroed before the PV product, and O is scaled by 1 / (1 - p) at the end.
-template <typename TR, int D, int BR, int BC, int NS, bool CAUSAL, bool BIG, bool DROP>
+// SPARSE: block-sparse attention. Key tiles whose 128 x 128 mask block is zero for every row of
+// the work-group are neither loaded nor computed; a wave skips the tiles its own mask row zeroes.
+// Rows with no allowed key give O = 0, LSE = -inf.
+template <typename TR, int D, int BR, int BC, int NS, bool CAUSAL, bool BIG, bool DROP, bool SPARSE>
 __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   using Cfg = FwdCfg<D, BR, BC, NS>;
   using vec8 = typename TR::vec8;
@@ -153,8 +158,9 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   const uint32_t head_bytes = BIG ? 0u : (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rK = make_rsrc(Kh, head_bytes);
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(Vh, head_bytes);
-  auto issue = [&](int j) {
-    uint8_t* st = smem + (j % NS) * Cfg::STAGE_B + w * 64 * 16;
+  // tile j into stage stg % NS (stg = j except for block-sparse runs, which skip tiles)
+  auto issue = [&](int j, int stg) {
+    uint8_t* st = smem + (stg % NS) * Cfg::STAGE_B + w * 64 * 16;
     if (!BIG && (j + 1) * BC <= N) {
       const uint32_t soff = (uint32_t)(j * BC) * (D * 2);
 #pragma unroll
@@ -180,7 +186,10 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   for (int b = 0; b < D / 32; ++b)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
-  float m_ref = -__builtin_inff();
+  // A row of a block-sparse run can meet a tile whose keys it cannot see before its first real
+  // one; a finite start keeps exp2(s*c - m_ref) at 0 there (not NaN), and the first real logit
+  // always outgrows it with a rescale factor of exactly 0. Dense rows see key 0 in tile 0.
+  float m_ref = SPARSE ? -3.402823466e38f : -__builtin_inff();
   float l_part = 0.f;
 
   const int tr_row = 4 * h + ((lane & 15) >> 2);
@@ -188,9 +197,9 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
 
   // S^T = K Q^T for tile j (BC/32 independent 32-key accumulator chains), masked on diagonal and
   // ragged tiles; returns the row max of the log2-domain logits.
-  auto scores = [&](int j, f32x16 (&s)[BC / 32]) {
+  auto scores = [&](int j, int stg, f32x16 (&s)[BC / 32]) {
     const int k0 = j * BC;
-    const uint8_t* Ks = smem + (j % NS) * Cfg::STAGE_B;
+    const uint8_t* Ks = smem + (stg % NS) * Cfg::STAGE_B;
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
@@ -235,8 +244,8 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   // P^T = exp2(s*c - m_ref) (masked scores are -inf and give 0), packed to 16-bit MFMA B
   // fragments (8 keys per 16-key chunk), then O^T += V^T P^T with V^T fragments from the
   // transposed LDS read (rows 16c + tr_row and +8).
-  auto softmax_pv = [&](int j, const f32x16 (&s)[BC / 32]) {
-    const uint8_t* Vs = smem + (j % NS) * Cfg::STAGE_B + TILE_B;
+  auto softmax_pv = [&](int j, int stg, const f32x16 (&s)[BC / 32]) {
+    const uint8_t* Vs = smem + (stg % NS) * Cfg::STAGE_B + TILE_B;
     const float neg_m = -m_ref;
     vec8 pf[BC / 16];
     float ls = 0.f;
@@ -287,45 +296,99 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   // done outside it and the loop resumes. Keeping the conditional rescale out of the loop body
   // keeps the accumulator in one set of registers (a join inside the loop made the compiler copy
   // all of it on every tile).
-  for (int t = 0; t < NS - 1 && t < n_kv; ++t) issue(t);
-  int j = 0;
   f32x16 s[BC / 32];
   float m_new = 0.f;
-  while (j < n_kv) {
-    bool grew = false;
-    for (; j < n_kv; ++j) {
-      // this wave's loads of tile j have landed (tiles j+1 .. j+NS-2 may still be in flight)
-      if (j + NS - 2 < n_kv) wait_vmcnt<(NS - 2) * Cfg::LPI>();
-      else wait_vmcnt<0>();
-      barrier_lds();  // ... and everyone's; stage (j - 1) % NS is no longer being read
-      if (j + NS - 1 < n_kv) issue(j + NS - 1);
-      if (!(wave_active && j * BC < wave_kv_end)) continue;
-      const float mx = scores(j, s);
-      m_new = fmaxf(m_ref, mx);
-      if (wave_any(m_new > m_ref + kRescaleSlack)) {
-        grew = true;
-        break;
+  if constexpr (!SPARSE) {
+    for (int t = 0; t < NS - 1 && t < n_kv; ++t) issue(t, t);
+    int j = 0;
+    while (j < n_kv) {
+      bool grew = false;
+      for (; j < n_kv; ++j) {
+        // this wave's loads of tile j have landed (tiles j+1 .. j+NS-2 may still be in flight)
+        if (j + NS - 2 < n_kv) wait_vmcnt<(NS - 2) * Cfg::LPI>();
+        else wait_vmcnt<0>();
+        barrier_lds();  // ... and everyone's; stage (j - 1) % NS is no longer being read
+        if (j + NS - 1 < n_kv) issue(j + NS - 1, j + NS - 1);
+        if (!(wave_active && j * BC < wave_kv_end)) continue;
+        const float mx = scores(j, j, s);
+        m_new = fmaxf(m_ref, mx);
+        if (wave_any(m_new > m_ref + kRescaleSlack)) {
+          grew = true;
+          break;
+        }
+        softmax_pv(j, j, s);
       }
-      softmax_pv(j, s);
+      if (!grew) break;
+      // Move the reference max of the rows that outgrew it, rescale their state, finish tile j.
+      const bool grow = m_new > m_ref + kRescaleSlack;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+      if (grow) m_ref = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
+      softmax_pv(j, j, s);
+      ++j;
     }
-    if (!grew) break;
-    // Move the reference max of the rows that outgrew it, rescale their state, finish tile j.
-    const bool grow = m_new > m_ref + kRescaleSlack;
-    const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
-    if (grow) m_ref = m_new;
-    l_part *= alpha;
+  } else {
+    // Block-sparse: the work-group visits the key tiles whose mask column is set for any of its
+    // mask rows, in order, two stages deep (stage = position in that sequence); each wave
+    // computes the ones its own mask row allows.
+    static_assert(NS == 2, "block-sparse runs use two stages");
+    const uint8_t* bm = a.bmask + (size_t)bh * a.nb * a.nb;
+    const int r_lo = q_base / 128, r_hi = min(a.nb, (q_base + BR + 127) / 128);
+    const int wave_row = min(q0, N - 1) / 128;
+    auto col = [&](int j) { return (j * BC) / 128; };
+    auto wg_on = [&](int j) {
+      bool on = false;
+      for (int r = r_lo; r < r_hi; ++r) on = on || bm[(size_t)r * a.nb + col(j)] != 0;
+      return on;
+    };
+    auto next = [&](int j) {
+      ++j;
+      while (j < n_kv && !wg_on(j)) ++j;
+      return j;
+    };
+    int j = next(-1), t = 0;
+    if (j < n_kv) issue(j, 0);
+    while (j < n_kv) {
+      bool grew = false;
+      int jn = j;
+      for (; j < n_kv; j = jn, ++t) {
+        wait_vmcnt<0>();
+        barrier_lds();
+        jn = next(j);
+        if (jn < n_kv) issue(jn, t + 1);
+        if (!(wave_active && j * BC < wave_kv_end && bm[(size_t)wave_row * a.nb + col(j)] != 0)) continue;
+        const float mx = scores(j, t, s);
+        m_new = fmaxf(m_ref, mx);
+        if (wave_any(m_new > m_ref + kRescaleSlack)) {
+          grew = true;
+          break;
+        }
+        softmax_pv(j, t, s);
+      }
+      if (!grew) break;
+      const bool grow = m_new > m_ref + kRescaleSlack;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+      if (grow) m_ref = m_new;
+      l_part *= alpha;
 #pragma unroll
-    for (int b = 0; b < D / 32; ++b)
+      for (int b = 0; b < D / 32; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
-    softmax_pv(j, s);
-    ++j;
+        for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
+      softmax_pv(j, t, s);
+      j = jn;
+      ++t;
+    }
   }
 
   if (!wave_active) return;
   const float l_tot = sum_halves(l_part);
   if (qrow >= N) return;
-  const float inv = (DROP ? a.drop.inv_keep : 1.0f) / l_tot;
+  float inv = (DROP ? a.drop.inv_keep : 1.0f) / l_tot;
+  if (SPARSE && !(l_tot > 0.f)) inv = 0.f;  // no allowed key: O = 0
   uint16_t* Orow = a.o + head + (size_t)qrow * D;
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
@@ -336,7 +399,8 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
       v2[1] = TR::pack2(acc[b][4 * jj + 2] * inv, acc[b][4 * jj + 3] * inv);
       *(u32x2*)(Orow + 32 * b + 8 * jj + 4 * h) = v2;
     }
-  if (h == 0) a.lse[(size_t)bh * N + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
+  if (h == 0)
+    a.lse[(size_t)bh * N + qrow] = (SPARSE && !(l_tot > 0.f)) ? -__builtin_inff() : (m_ref + __log2f(l_tot)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -521,7 +585,7 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel_f32(FwdArgsF32 a) {
 // ---------------------------------------------------------------------------------------------
 // Dispatch.
 
-template <typename TR, int D, int BR, int BC, int NS, bool DROP = false>
+template <typename TR, int D, int BR, int BC, int NS, bool DROP = false, bool SPARSE = false>
 hipError_t launch16(const FwdReq& r, hipStream_t st) {
   FwdArgs a;
   a.q = (const uint16_t*)r.q;
@@ -536,16 +600,18 @@ hipError_t launch16(const FwdReq& r, hipStream_t st) {
   a.neg_mask = r.scale < 0.f ? 0x80008000u : 0u;
   a.keep_mask = r.scale == 0.f ? 0u : 0xffffffffu;
   a.drop = r.drop;
+  a.bmask = r.bmask;
+  a.nb = (r.N + 127) / 128;
   const long long nblk = (long long)r.B * r.H * a.n_qtiles;
   const dim3 grid((unsigned)nblk), block(BR / 32 * 64);
   // buffer offsets are 32-bit: heads of 2 GiB or more take the 64-bit address path
   const bool big = (size_t)r.N * D * 2 >= ((size_t)1 << 31);
   if (r.causal) {
-    if (big) hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, true, true, DROP>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, true, false, DROP>), grid, block, 0, st, a);
+    if (big) hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, true, true, DROP, SPARSE>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, true, false, DROP, SPARSE>), grid, block, 0, st, a);
   } else {
-    if (big) hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, false, true, DROP>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, false, false, DROP>), grid, block, 0, st, a);
+    if (big) hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, false, true, DROP, SPARSE>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<TR, D, BR, BC, NS, false, false, DROP, SPARSE>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -573,10 +639,15 @@ hipError_t launch32(const FwdReq& r, hipStream_t st) {
 
 template <typename TR, int D>
 hipError_t launch16_tile(const FwdReq& r, hipStream_t st) {
-  if (r.dropout) {  // dropout instances exist for the default tiles only
-    if (D == 128 && r.Br == 256 && r.Bc == 128) return launch16<TR, D, 256, 128, 2, true>(r, st);
-    if (D == 64 && r.Br == 128 && r.Bc == 64) return launch16<TR, D, 128, 64, 2, true>(r, st);
-    return hipErrorInvalidValue;
+  // block-sparse and dropout instances exist for the default tile of each head dim only
+  if (r.bmask || r.dropout) {
+    if constexpr (D == 128) {
+      if (r.Br != 256 || r.Bc != 128) return hipErrorInvalidValue;
+      return r.bmask ? launch16<TR, D, 256, 128, 2, false, true>(r, st) : launch16<TR, D, 256, 128, 2, true>(r, st);
+    } else {
+      if (r.Br != 128 || r.Bc != 64) return hipErrorInvalidValue;
+      return r.bmask ? launch16<TR, D, 128, 64, 2, false, true>(r, st) : launch16<TR, D, 128, 64, 2, true>(r, st);
+    }
   }
   if (r.Br == 128 && r.Bc == 64) return launch16<TR, D, 128, 64, 2>(r, st);
   if (r.Br == 128 && r.Bc == 128) return launch16<TR, D, 128, 128, 2>(r, st);

@@ -21,6 +21,7 @@ struct FwdReq {
   int Br, Bc; // resolved tile shape (never 0 here)
   bool dropout = false;  // dropout on P with `drop` (default tiles, 16-bit types only)
   DropParams drop = {0u, 0u, 0u, 1.0f};
+  const uint8_t* bmask = nullptr;  // block mask [B*H][nb][nb], nb = ceil(N/128) (default tiles)
 };
 
 struct BwdReq {

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(L):
             "fattn_bwd_dv", "fattn_bwd_dk", "fattn_bwd_dq", "fattn_fwd_splitkv",
             "fattn_fwd_splitkv_workspace_size", "fattn_splitkv_num_splits", "fattn_fwd_partial",
             "fattn_combine", "fattn_fwd_kouter", "fattn_fwd_kouter_workspace_size",
-            "fattn_fwd_dropout", "fattn_bwd_dropout"} <= set(names)
+            "fattn_fwd_dropout", "fattn_bwd_dropout", "fattn_fwd_blocksparse"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
         assert getattr(fa, n) is not None
@@ -262,3 +262,15 @@ def test_bwd_dropout_rejects_bad_arguments(L, kw, status):
 def test_dropout_seed_is_64_bit(L):
     # a seed above 2^32 passes the host checks (rejected here only for the fake NULL output)
     assert fa.fattn_fwd_dropout(P[0], P[1], P[2], None, P[4], 1, 1, 16, 64, 0.1, 0, 2, 0.3, 2**63 + 5) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=None), -1), (dict(q=None), -1), (dict(dtype=0), -4), (dict(d=96), -3), (dict(N=0), -2),
+    (dict(causal=5), -12), (dict(scale=float("inf")), -7), (dict(o=MIS), -6), (dict(o=P[5]), -11),
+    (dict(lse=P[0]), -11),
+])
+def test_blocksparse_rejects_bad_arguments(L, kw, status):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], m=P[5], N=300, d=64, causal=0, dtype=2, scale=0.1)
+    a.update(kw)
+    assert fa.fattn_fwd_blocksparse(a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 2, a["N"], a["d"], a["scale"],
+                                    a["causal"], a["dtype"], a["m"]) == status
