@@ -11,14 +11,14 @@
 //
 // Three kernels, all in stream order:
 //  1. bwd_pre:   D = rowsum(dO * O) (float32 workspace), one pass over O and dO.
-//  2. bwd_dkdv:  one work-group per (b*h, 128-key tile), in two passes (dV, then dK); each of
-//               its 4 waves keeps 32 keys of K (and V) in registers and a float32 accumulator,
+//  2. bwd_dkdv:  one work-group per (b*h, 256-key tile), in two passes (dV, then dK); each of
+//               its 8 waves keeps 32 keys of K (and V) in registers and a float32 accumulator,
 //               while Q, dO tiles of 64 queries stream memory -> LDS, two stages deep. Scores are
 //               formed as S = Q K^T so that every lane owns ONE key: P and dS then serve directly
 //               as the MFMA A operand of dV += P^T dO and dK += dS^T Q, whose B operands (dO and
 //               Q with the query index as reduction index) come from the same LDS tiles through
 //               ds_read_b64_tr_b16.
-//  3. bwd_dq:    one work-group per (b*h, 128-query tile), the forward's layout: S^T = K Q^T and
+//  3. bwd_dq:    one work-group per (b*h, 256-query tile), the forward's layout: S^T = K Q^T and
 //               dP^T = V dO^T give each lane ONE query (its LSE and D are per-lane scalars);
 //               dQ^T += K^T dS^T takes K^T from the row-major K tile via the transposed read.
 // Every kernel writes its outputs once; there are no atomics, so results are deterministic.
@@ -125,7 +125,7 @@ __device__ inline int row_read_addr(int R, int c) {
 // ---------------------------------------------------------------------------------------------
 // 2. dK, dV.
 //
-// One work-group per (b*h, 128-key tile); each of its 4 waves keeps 32 keys of K and V in
+// One work-group per (b*h, 256-key tile); each of its 8 waves keeps 32 keys of K and V in
 // registers (MFMA B operands) and the float32 dK, dV accumulators. Tiles of 64 queries of Q and dO
 // go from memory straight into LDS (two stages), with the per-row log2-domain LSE and D beside
 // them. S = Q K^T and dP = dO V^T put ONE key in each lane, so P and dS serve directly as the A
@@ -134,9 +134,9 @@ __device__ inline int row_read_addr(int R, int c) {
 
 template <int D>
 struct DkdvCfg {
-  static constexpr int BKV = 128;               // keys per work-group (32 per wave)
+  static constexpr int BKV = 256;               // keys per work-group (32 per wave)
   static constexpr int BQ = 64;                 // queries per step
-  static constexpr int NT = 256;
+  static constexpr int NT = BKV / 32 * 64;
   static constexpr int CPR = D / 8;
   static constexpr int LPT = BQ * CPR / NT;     // 16-byte loads per thread per tile per tensor
   static constexpr int TILE_B = BQ * D * 2;     // bytes of one Q (or dO) tile
@@ -152,7 +152,7 @@ struct DkdvCfg {
 // DROP: dropout on P with mask M (Pd = P M / (1 - p)): the dV pass accumulates Pd^T dO, the dK
 // pass uses dS = P (dO V^T M / (1 - p) - D); D = rowsum(dO O) is unchanged.
 template <typename TR, int D, bool CAUSAL, bool BIG, int MODE, bool DROP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(DkdvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(BwdArgs a) {
   static_assert(MODE == 1 || MODE == 2, "dV pass or dK pass");
   constexpr bool DO_DV = MODE == 1, DO_DK = MODE == 2;
   using Cfg = DkdvCfg<D>;
@@ -405,16 +405,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 // ---------------------------------------------------------------------------------------------
 // 3. dQ.
 //
-// One work-group per (b*h, 128-query tile), the forward's layout: S^T = K Q^T and dP^T = V dO^T
+// One work-group per (b*h, 256-query tile), the forward's layout: S^T = K Q^T and dP^T = V dO^T
 // give each lane ONE query (its LSE and D are per-lane scalars); dQ^T += K^T dS^T takes K^T from
 // the K tile through the transposed read. K and V tiles of 64 keys stream memory -> LDS, two
 // stages deep.
 
 template <int D>
 struct DqCfg {
-  static constexpr int BQ = 128;              // queries per work-group (32 per wave)
+  static constexpr int BQ = 256;              // queries per work-group (32 per wave)
   static constexpr int BK = 64;               // keys per step
-  static constexpr int NT = 256;
+  static constexpr int NT = BQ / 32 * 64;
   static constexpr int CPR = D / 8;
   static constexpr int LPT = BK * CPR / NT;
   static constexpr int TILE_B = BK * D * 2;
@@ -424,7 +424,7 @@ struct DqCfg {
 
 // DROP: dS = P (dO V^T M / (1 - p) - D).
 template <typename TR, int D, bool CAUSAL, bool BIG, bool DROP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BwdArgs a) {
   using Cfg = DqCfg<D>;
   using vec8 = typename TR::vec8;
   constexpr int BQ = Cfg::BQ, BK = Cfg::BK, NT = Cfg::NT, CPR = Cfg::CPR, LPT = Cfg::LPT;
@@ -635,7 +635,7 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
   if (stage < 0 || stage == 1 || stage == 3 || stage == 4) {
     a.ntiles = (r.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
     dim3 g1((unsigned)(BH * a.ntiles));
-    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, g1, dim3(256), 0, st, a); };
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, g1, dim3(DkdvCfg<D>::NT), 0, st, a); };
     const bool dv_pass = stage != 4, dk_pass = stage != 3;
     if (r.causal) {
       if (dv_pass) big ? go(bwd_dkdv_kernel<TR, D, true, true, 1, DROP>) : go(bwd_dkdv_kernel<TR, D, true, false, 1, DROP>);
@@ -651,11 +651,11 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
     a.ntiles = (r.N + DqCfg<D>::BQ - 1) / DqCfg<D>::BQ;
     dim3 g2((unsigned)(BH * a.ntiles));
     if (r.causal) {
-      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, true, DROP>), g2, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, false, DROP>), g2, dim3(256), 0, st, a);
+      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, true, DROP>), g2, dim3(DqCfg<D>::NT), 0, st, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, false, DROP>), g2, dim3(DqCfg<D>::NT), 0, st, a);
     } else {
-      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, true, DROP>), g2, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, false, DROP>), g2, dim3(256), 0, st, a);
+      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, true, DROP>), g2, dim3(DqCfg<D>::NT), 0, st, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, false, DROP>), g2, dim3(DqCfg<D>::NT), 0, st, a);
     }
     e = hipGetLastError();
   }
