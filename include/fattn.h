@@ -106,7 +106,8 @@ int fattn_fwd_dropout(const void* q, const void* k, const void* v, void* o, floa
  * [128 r, 128 r + 128) and keys [128 c, 128 c + 128); nonzero = computed. Scores outside allowed
  * blocks (and above the diagonal when causal) are -inf; a row with no allowed key gets O = 0 and
  * LSE = -inf. Key tiles whose blocks are zero for a whole work-group are neither read nor
- * computed. f16/bf16 only; default tile shape; same other conventions as fattn_fwd.
+ * computed. f16/bf16 only; runs with 128 x 64 tiles (one mask row per work-group); same other
+ * conventions as fattn_fwd.
  */
 int fattn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
                           int B, int H, int N, int d, float scale, int causal, int dtype,

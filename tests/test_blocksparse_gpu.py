@@ -1,5 +1,5 @@
 """Block-sparse forward against the float64 block-sparse oracle (same fp16/bf16 tolerances as the
-dense forward), plus its reduction to the dense kernel for an all-ones mask (bit for bit)."""
+dense forward), plus its reduction to the dense kernel on the same tile shape for an all-ones mask (bit for bit)."""
 import math
 
 import numpy as np
@@ -66,7 +66,7 @@ def test_blocksparse_all_ones_is_the_dense_kernel(d, causal):
     nb = (N + 127) // 128
     m = torch.ones((2, 2, nb, nb), dtype=torch.uint8, device="cuda")
     o1, l1 = fa.forward_blocksparse(q, k, v, m, causal=causal)
-    o2, l2 = fa.forward(q, k, v, causal=causal)
+    o2, l2 = fa.forward(q, k, v, causal=causal, Br=128, Bc=64)  # the block-sparse path's tiles
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
