@@ -280,10 +280,10 @@ def main(argv=None):
     # 2*N^2*d per head: forward 2 (S, PV); the dV pass 2 (S, dV); the dK pass 3 (S, dP, dK);
     # dQ 3 (S, dP, dQ).
     kernels = {
-        "fwd": ("fwd_kernel", f_fwd, 1024 * 256, "fwd_kernel<Bf16, 128, 256, 128, 2, true, false>"),
-        "dv": ("bwd_dkdv_kernel", f_fwd, 1024 * 256, "bwd_dkdv_kernel<Bf16, 128, true, false, 1>"),
-        "dk": ("bwd_dkdv_kernel", 1.5 * f_fwd, 1024 * 256, "bwd_dkdv_kernel<Bf16, 128, true, false, 2>"),
-        "dq": ("bwd_dq_kernel", 1.5 * f_fwd, 1024 * 256, "bwd_dq_kernel<Bf16, 128, true, false>"),
+        "fwd": ("fwd_kernel", f_fwd, 1024 * 256, "fwd_kernel<Bf16, 128, 256, 128, 2, true, false, false, false>"),
+        "dv": ("bwd_dkdv_kernel", f_fwd, 1024 * 256, "bwd_dkdv_kernel<Bf16, 128, true, false, 1, false>"),
+        "dk": ("bwd_dkdv_kernel", 1.5 * f_fwd, 1024 * 256, "bwd_dkdv_kernel<Bf16, 128, true, false, 2, false>"),
+        "dq": ("bwd_dq_kernel", 1.5 * f_fwd, 1024 * 256, "bwd_dq_kernel<Bf16, 128, true, false, false>"),
     }
     dom = max(kernels, key=lambda k_: ms[k_])
     name, fl, grid, sig = kernels[dom]
