@@ -100,6 +100,36 @@ def cpu_oracle_baseline(budget_s: float = 20.0):
                       f"non-causal work, but is credited the causal FLOP count)"}
 
 
+SWEEP_N = (1024, 2048, 4096, 8192, 16384)
+
+
+def n_sweep(torch, fa):
+    """Forward at N = 1024 .. 16384 (B=1, H=16, d=128, bf16), causal and non-causal: three launches
+    each (for counter runs) and a timed block each; then a 256 MiB + 256 MiB calibration copy."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2024)
+    out = {"workload": "forward, B=1 H=16 d=128 bf16, N sweep", "runs": []}
+    for N in SWEEP_N:
+        q, k, v = (torch.randn(1, 16, N, 128, device="cuda", dtype=torch.bfloat16, generator=gen)
+                   for _ in range(3))
+        o, lse = torch.empty_like(q), torch.empty(1, 16, N, device="cuda")
+        for causal in (False, True):
+            for _ in range(3):
+                fa.forward(q, k, v, causal=causal, out=o, lse=lse)
+            torch.cuda.synchronize()
+            ms = _time_calls(lambda: fa.forward(q, k, v, causal=causal, out=o, lse=lse), 10, 2, torch)
+            out["runs"].append({"N": N, "causal": causal, "ms": round(ms, 4),
+                                "tflops": round(flops_fwd(1, 16, N, 128, causal) / (ms * 1e-3) / 1e12, 1)})
+        del q, k, v, o, lse
+    src = torch.ones(128 * 2**20, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +143,10 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB read + 256 MiB write elementwise copy, so HBM "
                          "byte counters can be scaled by a kernel of known traffic")
+    ap.add_argument("--n-sweep", action="store_true",
+                    help="only run the forward at N = 1024 .. 16384 (B=1, H=16, d=128, bf16, causal and "
+                         "non-causal) a few times each, plus the calibration copy, for the HBM-bytes-vs-N "
+                         "counters; prints one JSON line with the per-N times")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the kernels shard over (batch, head) with no "
@@ -125,6 +159,8 @@ def main(argv=None):
     from io_aware_tiled_fattn_amd import profiling
 
     fa.lib()
+    if a.n_sweep:
+        return n_sweep(torch, fa)
     w5, w3 = fi.WORKLOADS[5], fi.WORKLOADS[3]
     B, H, N, d = w5.shape
 

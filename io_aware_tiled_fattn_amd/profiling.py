@@ -39,6 +39,17 @@ COMMANDS = {
 }
 
 
+# HBM bytes versus N for the forward (spec evidence that traffic stays O(N d)).
+SWEEP_COMMANDS = {
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {run}/fetch -o run -- "
+             "python -u bench.py --n-sweep",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {run}/write -o run -- "
+             "python -u bench.py --n-sweep",
+    "mfma": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d {run}/mfma -o run -- "
+            "python -u bench.py --n-sweep",
+}
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
@@ -174,6 +185,67 @@ def write_summaries(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
     return stats, tr
 
 
+def _fit_exponent(ns, ys):
+    """Least-squares slope of log(y) against log(N)."""
+    import math
+    xs = [math.log(n) for n in ns]
+    ls = [math.log(y) for y in ys]
+    mx, my = sum(xs) / len(xs), sum(ls) / len(ls)
+    return sum((x - mx) * (y - my) for x, y in zip(xs, ls)) / sum((x - mx) ** 2 for x in xs)
+
+
+def write_sweep(run_dir, prof_dir, times=None, bh=16, d=128):
+    """profiles/hbm_scaling_fwd_bh16d128_bf16.md from the three sweep runs (fetch, write, mfma)."""
+    tr, fc, wc = traffic(run_dir)
+    busy, bmeta = _counter_per_dispatch(_find(run_dir, "mfma", "counter_collection.csv"), "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui, _ = _counter_per_dispatch(_find(run_dir, "mfma", "counter_collection.csv"), "GRBM_GUI_ACTIVE")
+    mfma = collections.defaultdict(list)
+    for k, v in busy.items():
+        name, grid = bmeta[k]
+        # GRBM_GUI_ACTIVE is summed over the 8 XCDs; 1024 SIMDs in all
+        if gui.get(k):
+            mfma[(name, grid)].append(v / (gui[k] / 8.0 * 1024.0))
+    rows = []
+    for t in tr:
+        if not t["kernel"].startswith("fwd_kernel"):
+            continue
+        n = t["grid"] // 512 * 256 // bh  # 256 query rows per 512-thread work-group
+        causal = ", true, false, false, false>" in t["kernel"]
+        busy_f = mfma.get((t["kernel"], t["grid"]))
+        rows.append({"N": n, "causal": causal, "fetch": t["fetch_bytes"], "write": t["write_bytes"],
+                     "mfma_busy": sum(busy_f) / len(busy_f) if busy_f else None})
+    rows.sort(key=lambda r: (r["causal"], r["N"]))
+    lines = ["# HBM bytes versus N — forward, B=1 H=16 d=128 bf16 (256 x 128 tiles)\n",
+             "Commands (from the repository root, on the GPU box; RUN is an output folder):\n"]
+    for key in ("fetch", "write", "mfma"):
+        lines.append("    " + SWEEP_COMMANDS[key].format(run="RUN"))
+    lines += ["", f"Counters calibrated on a 256 MiB + 256 MiB copy (FETCH_SIZE x{fc:.3f}, WRITE_SIZE x{wc:.3f}). "
+              "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs).", "",
+              "| causal | N | HBM read MiB | HBM written MiB | Q+K+V+O+LSE MiB | N x N score matrix MiB (bf16) | MFMA busy |",
+              "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        io = (4 * r["N"] * d * 2 + 4 * r["N"]) * bh / 2**20
+        nn = r["N"] * r["N"] * 2 * bh / 2**20
+        mb = f"{r['mfma_busy']:.1%}" if r["mfma_busy"] is not None else "—"
+        lines.append(f"| {r['causal']} | {r['N']} | {r['fetch'] / 2**20:.1f} | {r['write'] / 2**20:.1f} | "
+                     f"{io:.1f} | {nn:.0f} | {mb} |")
+    lines.append("")
+    for causal in (False, True):
+        sel = [r for r in rows if r["causal"] == causal]
+        if len(sel) >= 2:
+            e = _fit_exponent([r["N"] for r in sel], [r["fetch"] + r["write"] for r in sel])
+            lines.append(f"Fitted exponent of HBM bytes in N (causal={causal}): {e:.3f} "
+                         f"(the score matrix would grow with exponent 2).")
+    if times:
+        lines += ["", "Times from the same command's timed blocks (HIP events):", "",
+                  "| causal | N | ms | TFLOP/s |", "|---|---|---|---|"]
+        for t in times:
+            lines.append(f"| {t['causal']} | {t['N']} | {t['ms']} | {t['tflops']} |")
+    with open(os.path.join(prof_dir, "hbm_scaling_fwd_bh16d128_bf16.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return rows
+
+
 def load_traffic(prof_dir):
     """Per-(kernel, grid) HBM bytes if they were measured on the current kernel sources."""
     path = os.path.join(prof_dir, "traffic.json")
@@ -187,6 +259,14 @@ def load_traffic(prof_dir):
 
 
 if __name__ == "__main__":
+    if sys.argv[1] == "sweep":
+        times = None
+        if len(sys.argv) > 4:
+            with open(sys.argv[4]) as f:
+                times = json.loads(f.read().strip().splitlines()[-1])["runs"]
+        for r in write_sweep(sys.argv[2], sys.argv[3], times):
+            print(r)
+        sys.exit(0)
     run = sys.argv[1]
     prof = sys.argv[2] if len(sys.argv) > 2 else os.path.join(os.path.dirname(HERE), "profiles")
     s, t = write_summaries(run, prof)
