@@ -217,8 +217,6 @@ def main(argv=None):
         "fwd": T(lambda: fa.forward(q, k, v, causal=True, out=o, lse=lse)),
         "pre": T(st((0,))),
         "dkdv": T(st((1,))),
-        "dv": T(st((3,))),
-        "dk": T(st((4,))),
         "dq": T(st((2,))),
         "bwd": T(lambda: fa.backward(q, k, v, o, do, lse, causal=True, workspace=ws)),
     }
@@ -313,12 +311,11 @@ def main(argv=None):
     value = tf(f_step, ms_step)
 
     # Algorithmic FLOPs per launch of each matmul kernel (causal halves every GEMM), each GEMM
-    # 2*N^2*d per head: forward 2 (S, PV); the dV pass 2 (S, dV); the dK pass 3 (S, dP, dK);
-    # dQ 3 (S, dP, dQ).
+    # 2*N^2*d per head: forward 2 (S, PV); dK/dV 4 (S, dP, dV, dK); dQ 3 (S, dP, dQ). Grids in
+    # threads: 512 per work-group; forward and dQ 256 rows per group, dK/dV 128 keys.
     kernels = {
         "fwd": ("fwd_kernel", f_fwd, 1024 * 256, "fwd_kernel<Bf16, 128, 256, 128, 2, true, false, false, false>"),
-        "dv": ("bwd_dkdv_kernel", f_fwd, 1024 * 256, "bwd_dkdv_kernel<Bf16, 128, true, false, 1, false>"),
-        "dk": ("bwd_dkdv_kernel", 1.5 * f_fwd, 1024 * 256, "bwd_dkdv_kernel<Bf16, 128, true, false, 2, false>"),
+        "dkdv": ("bwd_dkdv_pair_kernel", 2 * f_fwd, 1024 * 512, "bwd_dkdv_pair_kernel<Bf16, 128, true, false, false>"),
         "dq": ("bwd_dq_kernel", 1.5 * f_fwd, 1024 * 256, "bwd_dq_kernel<Bf16, 128, true, false, false>"),
     }
     dom = max(kernels, key=lambda k_: ms[k_])

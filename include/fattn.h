@@ -151,10 +151,8 @@ int fattn_bwd_dropout(const void* q, const void* k, const void* v, const void* o
  * float32 [B,H,N] row vector D = rowsum(dO * O) (the first bytes of fattn_bwd's workspace).
  *   fattn_bwd_preprocess: reads o, dO; writes dvec.
  *   fattn_bwd_dkdv:       reads q, k, v, dO, lse, dvec; writes dk, dv (per key tile, recomputing
- *                         P = exp(S - LSE) for every query tile on or below the diagonal). It runs
- *                         as two passes over the query tiles, fattn_bwd_dv then fattn_bwd_dk:
- *   fattn_bwd_dv:         reads q, k, dO, lse (v and dvec are checked but unused); writes dv.
- *   fattn_bwd_dk:         reads q, k, v, dO, lse, dvec; writes dk.
+ *                         P = exp(S - LSE) once for every query tile on or below the diagonal;
+ *                         dS = P (dP - D) takes P as rounded to the input type for dV = P^T dO).
  *   fattn_bwd_dq:         reads q, k, v, dO, lse, dvec; writes dq (per query tile).
  */
 int fattn_bwd_preprocess(const void* o, const void* dO, float* dvec, int B, int H, int N, int d,
@@ -162,12 +160,6 @@ int fattn_bwd_preprocess(const void* o, const void* dO, float* dvec, int B, int 
 int fattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                    const float* dvec, void* dk, void* dv, int B, int H, int N, int d, float scale,
                    int causal, int dtype, void* stream);
-int fattn_bwd_dv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                 const float* dvec, void* dv, int B, int H, int N, int d, float scale, int causal,
-                 int dtype, void* stream);
-int fattn_bwd_dk(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                 const float* dvec, void* dk, int B, int H, int N, int d, float scale, int causal,
-                 int dtype, void* stream);
 int fattn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                  const float* dvec, void* dq, int B, int H, int N, int d, float scale, int causal,
                  int dtype, void* stream);

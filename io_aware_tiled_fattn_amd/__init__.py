@@ -5,8 +5,8 @@ C ABI declared in include/fattn.h. PyTorch is used to allocate device memory and
 stream; there is no CPU or PyTorch fallback, and a missing library raises.
 
 Low-level names mirror the C entry points (``fattn_fwd``, ``fattn_fwd_tiled``, ``fattn_bwd``,
-``fattn_bwd_workspace_size``, ``fattn_bwd_preprocess``, ``fattn_bwd_dkdv``, ``fattn_bwd_dv``,
-``fattn_bwd_dk``, ``fattn_bwd_dq``, ``fattn_fwd_splitkv``, ``fattn_fwd_splitkv_workspace_size``,
+``fattn_bwd_workspace_size``, ``fattn_bwd_preprocess``, ``fattn_bwd_dkdv``, ``fattn_bwd_dq``,
+``fattn_fwd_splitkv``, ``fattn_fwd_splitkv_workspace_size``,
 ``fattn_splitkv_num_splits``, ``fattn_fwd_partial``, ``fattn_combine``, ``fattn_fwd_kouter``,
 ``fattn_fwd_kouter_workspace_size``, ``fattn_fwd_dropout``, ``fattn_bwd_dropout``,
 ``fattn_fwd_blocksparse``,
@@ -23,7 +23,7 @@ import os
 __all__ = [
     "FATTN_F32", "FATTN_F16", "FATTN_BF16", "FattnError", "lib", "library_path",
     "fattn_fwd", "fattn_fwd_tiled", "fattn_bwd", "fattn_bwd_workspace_size", "fattn_strerror",
-    "fattn_bwd_preprocess", "fattn_bwd_dkdv", "fattn_bwd_dv", "fattn_bwd_dk", "fattn_bwd_dq",
+    "fattn_bwd_preprocess", "fattn_bwd_dkdv", "fattn_bwd_dq",
     "fattn_version", "forward", "backward", "backward_stages", "dtype_code",
     "fattn_fwd_splitkv", "fattn_fwd_splitkv_workspace_size", "fattn_splitkv_num_splits",
     "fattn_fwd_partial", "fattn_combine", "forward_splitkv", "forward_partial", "combine",
@@ -70,9 +70,8 @@ def lib():
     L.fattn_bwd_preprocess.restype = i
     L.fattn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     L.fattn_bwd_dkdv.restype = i
-    for name in ("fattn_bwd_dv", "fattn_bwd_dk", "fattn_bwd_dq"):
-        getattr(L, name).argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
-        getattr(L, name).restype = i
+    L.fattn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    L.fattn_bwd_dq.restype = i
     L.fattn_splitkv_num_splits.argtypes = [i, i, i, i, i]
     L.fattn_splitkv_num_splits.restype = i
     L.fattn_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i, i]
@@ -129,14 +128,6 @@ def fattn_bwd_preprocess(o, dO, dvec, B, H, N, d, dtype, stream=None) -> int:
 
 def fattn_bwd_dkdv(q, k, v, dO, lse, dvec, dk, dv, B, H, N, d, scale, causal, dtype, stream=None) -> int:
     return lib().fattn_bwd_dkdv(q, k, v, dO, lse, dvec, dk, dv, B, H, N, d, scale, causal, dtype, stream)
-
-
-def fattn_bwd_dv(q, k, v, dO, lse, dvec, dv, B, H, N, d, scale, causal, dtype, stream=None) -> int:
-    return lib().fattn_bwd_dv(q, k, v, dO, lse, dvec, dv, B, H, N, d, scale, causal, dtype, stream)
-
-
-def fattn_bwd_dk(q, k, v, dO, lse, dvec, dk, B, H, N, d, scale, causal, dtype, stream=None) -> int:
-    return lib().fattn_bwd_dk(q, k, v, dO, lse, dvec, dk, B, H, N, d, scale, causal, dtype, stream)
 
 
 def fattn_bwd_dq(q, k, v, dO, lse, dvec, dq, B, H, N, d, scale, causal, dtype, stream=None) -> int:
@@ -297,9 +288,8 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, stre
 
 def backward_stages(q, k, v, o, do, lse, dq, dk, dv, dvec, causal=False, scale=None, stream=None,
                     stages=(0, 1, 2)):
-    """Run the chosen stages of the backward (0: D = rowsum(dO*O), 1: dK/dV, 2: dQ, and the two
-    passes of stage 1 on their own: 3: dV, 4: dK) into preallocated outputs; ``dvec`` is a float32
-    [B, H, N] device tensor."""
+    """Run the chosen stages of the backward (0: D = rowsum(dO*O), 1: dK/dV, 2: dQ) into
+    preallocated outputs; ``dvec`` is a float32 [B, H, N] device tensor."""
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -316,10 +306,6 @@ def backward_stages(q, k, v, o, do, lse, dq, dk, dv, dvec, causal=False, scale=N
             st = fattn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
                               dvec.data_ptr(), dq.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
                               code, s)
-        elif stage in (3, 4):
-            fn, out = (fattn_bwd_dv, dv) if stage == 3 else (fattn_bwd_dk, dk)
-            st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                    dvec.data_ptr(), out.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), code, s)
         else:
             raise ValueError(f"unknown backward stage {stage}")
         if st != 0:

@@ -300,26 +300,6 @@ int fattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, 
   return launch_status(fattn::launch_bwd(r, (hipStream_t)stream, 1));
 }
 
-int fattn_bwd_dv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                 const float* dvec, void* dv, int B, int H, int N, int d, float scale, int causal,
-                 int dtype, void* stream) {
-  int st = check_stage(q, k, v, dO, lse, dvec, dv, nullptr, B, H, N, d, scale, causal, dtype);
-  if (st != FATTN_OK) return st;
-  fattn::BwdReq r{q, k, v, nullptr, dO, lse, nullptr, nullptr, dv, B, H, N, d, scale, causal, dtype,
-                  (float*)dvec};
-  return launch_status(fattn::launch_bwd(r, (hipStream_t)stream, 3));
-}
-
-int fattn_bwd_dk(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                 const float* dvec, void* dk, int B, int H, int N, int d, float scale, int causal,
-                 int dtype, void* stream) {
-  int st = check_stage(q, k, v, dO, lse, dvec, dk, nullptr, B, H, N, d, scale, causal, dtype);
-  if (st != FATTN_OK) return st;
-  fattn::BwdReq r{q, k, v, nullptr, dO, lse, nullptr, dk, nullptr, B, H, N, d, scale, causal, dtype,
-                  (float*)dvec};
-  return launch_status(fattn::launch_bwd(r, (hipStream_t)stream, 4));
-}
-
 int fattn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                  const float* dvec, void* dq, int B, int H, int N, int d, float scale, int causal,
                  int dtype, void* stream) {

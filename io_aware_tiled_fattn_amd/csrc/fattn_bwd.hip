@@ -11,13 +11,14 @@
 //
 // Three kernels, all in stream order:
 //  1. bwd_pre:   D = rowsum(dO * O) (float32 workspace), one pass over O and dO.
-//  2. bwd_dkdv:  one work-group per (b*h, 256-key tile), in two passes (dV, then dK); each of
-//               its 8 waves keeps 32 keys of K (and V) in registers and a float32 accumulator,
-//               while Q, dO tiles of 64 queries stream memory -> LDS, two stages deep. Scores are
-//               formed as S = Q K^T so that every lane owns ONE key: P and dS then serve directly
-//               as the MFMA A operand of dV += P^T dO and dK += dS^T Q, whose B operands (dO and
-//               Q with the query index as reduction index) come from the same LDS tiles through
-//               ds_read_b64_tr_b16.
+//  2. bwd_dkdv_pair: one work-group per (b*h, 128-key tile); waves p and p + 4 share 32 keys:
+//               the first keeps K in registers and accumulates dV (S, P, dV += P^T dO), the
+//               second keeps V and accumulates dK (dP, dS, dK += dS^T Q), taking P from the first
+//               through LDS, one query tile behind it. Q, dO tiles of 64 queries stream
+//               memory -> LDS, three stages deep. Scores are formed as S = Q K^T so that every
+//               lane owns ONE key: P and dS then serve directly as the MFMA A operand of the
+//               second product, whose B operand (dO or Q with the query index as reduction
+//               index) comes from the same LDS tiles through ds_read_b64_tr_b16.
 //  3. bwd_dq:    one work-group per (b*h, 256-query tile), the forward's layout: S^T = K Q^T and
 //               dP^T = V dO^T give each lane ONE query (its LSE and D are per-lane scalars);
 //               dQ^T += K^T dS^T takes K^T from the row-major K tile via the transposed read.
@@ -123,47 +124,63 @@ __device__ inline int row_read_addr(int R, int c) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// 2. dK, dV.
+// 2. dK, dV in one pass, by wave pairs.
 //
-// One work-group per (b*h, 256-key tile); each of its 8 waves keeps 32 keys of K and V in
-// registers (MFMA B operands) and the float32 dK, dV accumulators. Tiles of 64 queries of Q and dO
-// go from memory straight into LDS (two stages), with the per-row log2-domain LSE and D beside
-// them. S = Q K^T and dP = dO V^T put ONE key in each lane, so P and dS serve directly as the A
-// operand of dV += P^T dO and dK += dS^T Q, whose B operands (dO and Q with the query index as
-// reduction index) come from the same LDS tiles through ds_read_b64_tr_b16.
+// One work-group per (b*h, 128-key tile) of 8 waves; waves p and p + 4 (which share a SIMD) own
+// the same 32 keys. Wave p ("A") keeps K in registers and accumulates dV: S = Q K^T,
+// P = exp(S - LSE), dV += P^T dO. Wave p + 4 ("B") keeps V and accumulates dK: dP = dO V^T,
+// dS = P (dP - D), dK += dS^T Q, taking P from A through LDS (16-bit, as rounded for the dV
+// product). B works one query tile behind A, so the two never wait for each other inside a
+// tile: while A runs tile i, B runs tile i - 1; the tiles i - 1, i and the one being fetched
+// (i + 1) sit in three LDS stages, and P goes through two exchange buffers. S is computed once
+// per (query, key) pair, and each wave holds one accumulator and one operand set, so two waves
+// share every SIMD and one wave's VALU work overlaps the other's MFMAs.
 
 template <int D>
-struct DkdvCfg {
-  static constexpr int BKV = 256;               // keys per work-group (32 per wave)
-  static constexpr int BQ = 64;                 // queries per step
-  static constexpr int NT = BKV / 32 * 64;
+struct PairCfg {
+  static constexpr int BKV = 128;               // keys per work-group (32 per wave pair)
+  static constexpr int BQ = 64;                 // queries per tile
+  static constexpr int NT = 512;                // 8 waves
   static constexpr int CPR = D / 8;
   static constexpr int LPT = BQ * CPR / NT;     // 16-byte loads per thread per tile per tensor
   static constexpr int TILE_B = BQ * D * 2;     // bytes of one Q (or dO) tile
   static constexpr int ROWS_B = 2 * BQ * 4;     // LSE (log2 domain) then D, float32
   static constexpr int STAGE_B = 2 * TILE_B + ROWS_B;
-  static_assert(BQ * CPR % NT == 0, "tile split");
+  static constexpr int NSTG = 3;
+  static constexpr int XBUF_B = 4 * (BQ / 32) * 2 * 64 * 16;  // P of one tile: pairs x blocks x halves x lanes x 16 B
+  static constexpr int LDS_B = NSTG * STAGE_B + 2 * XBUF_B;
+  static_assert(BQ * CPR % NT == 0 && LPT >= 1, "tile split");
+  static_assert(LDS_B <= 160 * 1024, "LDS");
 };
 
-// MODE 1 accumulates dV only (S, P, dV += P^T dO: 2 GEMMs), MODE 2 dK only (S, dP, dS,
-// dK += dS^T Q: 3 GEMMs). The two passes recompute S, one GEMM more than a fused pass, but each
-// holds half the accumulators: both fit in 256 registers, so two waves share every SIMD and their
-// MFMA and VALU work overlaps (a fused pass needs ~300 registers and runs one wave per SIMD).
-// DROP: dropout on P with mask M (Pd = P M / (1 - p)): the dV pass accumulates Pd^T dO, the dK
-// pass uses dS = P (dO V^T M / (1 - p) - D); D = rowsum(dO O) is unchanged.
-template <typename TR, int D, bool CAUSAL, bool BIG, int MODE, bool DROP>
-__global__ __launch_bounds__(DkdvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(BwdArgs a) {
-  static_assert(MODE == 1 || MODE == 2, "dV pass or dK pass");
-  constexpr bool DO_DV = MODE == 1, DO_DK = MODE == 2;
-  using Cfg = DkdvCfg<D>;
+template <typename TR>
+__device__ inline void unpack2(uint32_t u, float& x, float& y);
+template <>
+__device__ inline void unpack2<Bf16>(uint32_t u, float& x, float& y) {
+  x = __uint_as_float(u << 16);
+  y = __uint_as_float(u & 0xffff0000u);
+}
+template <>
+__device__ inline void unpack2<F16>(uint32_t u, float& x, float& y) {
+  const f32x2v f = __builtin_convertvector(__builtin_bit_cast(f16x2v, u), f32x2v);
+  x = f[0];
+  y = f[1];
+}
+
+template <typename TR, int D, bool CAUSAL, bool BIG, bool DROP>
+__global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_pair_kernel(BwdArgs a) {
+  using Cfg = PairCfg<D>;
   using vec8 = typename TR::vec8;
   constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, NT = Cfg::NT, CPR = Cfg::CPR, LPT = Cfg::LPT;
-  constexpr int TILE_B = Cfg::TILE_B;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * Cfg::STAGE_B];
+  constexpr int TILE_B = Cfg::TILE_B, NSTG = Cfg::NSTG;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS_B];
+  uint8_t* const xbuf = smem + NSTG * Cfg::STAGE_B;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const bool role_a = w < 4;
+  const int pair = w & 3;
   const int h = lane >> 5;
   const int lr = lane & 31;
   const int N = a.N;
@@ -175,37 +192,31 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
   const uint16_t* __restrict__ Qh = a.q + head;
   const uint16_t* __restrict__ dOh = a.dO + head;
 
-  const int key0 = jt * BKV + 32 * w;  // first key of this wave
-  const int key = key0 + lr;           // this lane's key
+  const int key0 = jt * BKV + 32 * pair;  // first key of this wave pair
+  const int key = key0 + lr;              // this lane's key
   const bool wave_active = key0 < N;
 
-  // K and V fragments as MFMA B operands: lane holds X[key][16s + 8h .. +7].
-  vec8 kf[D / 16], vf[D / 16];
+  // MFMA B operand of the first product: K for A (S = Q K^T), V for B (dP = dO V^T);
+  // lane holds X[key][16s + 8h .. +7].
+  vec8 xf[D / 16];
+  {
+    const uint16_t* src = (role_a ? a.k : a.v) + head;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
-    if (key < N) {
-      kr = *(const u32x4*)(a.k + head + (size_t)key * D + 16 * s + 8 * h);
-      vr = *(const u32x4*)(a.v + head + (size_t)key * D + 16 * s + 8 * h);
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 r = {0u, 0u, 0u, 0u};
+      if (key < N) r = *(const u32x4*)(src + (size_t)key * D + 16 * s + 8 * h);
+      xf[s] = bitcast<vec8>(r);
     }
-    kf[s] = bitcast<vec8>(kr);
-    vf[s] = bitcast<vec8>(vr);
   }
-
-  f32x16 adk[D / 32], adv[D / 32];
+  f32x16 acc[D / 32];  // dV (A) or dK (B)
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      adk[b][e] = 0.f;
-      adv[b][e] = 0.f;
-    }
+    for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
 
   const int n_qt = (N + BQ - 1) / BQ;
   const int i_begin = CAUSAL ? (jt * BKV) / BQ : 0;
 
-  // Load i of this thread fills LDS chunk i*NT + tid of a Q (dO) tile with the source chunk
-  // (chunk % CPR) ^ swz_dual(row) of row chunk / CPR.
   uint32_t off[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
@@ -216,8 +227,9 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
   const uint32_t head_bytes = BIG ? 0u : (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Qh, head_bytes);
   const __amdgpu_buffer_rsrc_t rdO = make_rsrc(dOh, head_bytes);
+  auto stage = [&](int i) { return smem + (i % NSTG) * Cfg::STAGE_B; };
   auto issue = [&](int i) {
-    uint8_t* st = smem + (i & 1) * Cfg::STAGE_B + w * 64 * 16;
+    uint8_t* st = stage(i) + w * 64 * 16;
     if (!BIG && (i + 1) * BQ <= N) {
       const uint32_t soff = (uint32_t)(i * BQ) * (D * 2);
 #pragma unroll
@@ -226,8 +238,8 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
         buffer_lds16(rdO, st + TILE_B + t * NT * 16, off[t], soff);
       }
     } else {
-      // ragged last tile (or a huge head): rows past the end repeat row N - 1; their P and dS
-      // are zeroed below, so they add nothing
+      // ragged last tile (or a huge head): rows past the end repeat row N - 1; A masks them
+      // (P = 0), so B's dS is 0 there as well
 #pragma unroll
       for (int t = 0; t < LPT; ++t) {
         const size_t src_row = (size_t)min(i * BQ + (t * NT + tid) / CPR, N - 1) * (D * 2);
@@ -237,7 +249,6 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
       }
     }
   };
-  // per-query LSE (log2 domain) and D of tile i: loaded into registers, stored after the compute
   float lr2 = 0.f, dvr = 0.f;
   auto load_rows = [&](int i) {
     if (tid < BQ) {
@@ -248,13 +259,12 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
   };
   auto store_rows = [&](int i) {
     if (tid < BQ) {
-      float* rows = (float*)(smem + (i & 1) * Cfg::STAGE_B + 2 * TILE_B);
+      float* rows = (float*)(stage(i) + 2 * TILE_B);
       rows[tid] = lr2;
       rows[BQ + tid] = dvr;
     }
   };
 
-  // transposed-read coordinates: rows 16c + tr_row (+8), element column 32b + tr_col
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
@@ -263,129 +273,138 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
     issue(i_begin);
     store_rows(i_begin);
   }
-  for (int i = i_begin; i < n_qt; ++i) {
+  // iteration it: A runs tile it, B runs tile it - 1; the last iteration is B's alone
+  for (int it = i_begin; it <= n_qt; ++it) {
     wait_vmcnt<0>();
     barrier_lds();
-    if (i + 1 < n_qt) {
-      load_rows(i + 1);  // plain loads first, so waiting for them does not wait for the tiles
-      issue(i + 1);
+    if (it + 1 < n_qt) {
+      load_rows(it + 1);
+      issue(it + 1);
     }
+    const int i = role_a ? it : it - 1;
     const int q_base = i * BQ;
-    // causal: the whole tile lies above this wave's keys -> P = 0, nothing to add
-    if (wave_active && !(CAUSAL && q_base + BQ - 1 < key0)) {
-      const uint8_t* Qs = smem + (i & 1) * Cfg::STAGE_B;
+    const bool mine = role_a ? it < n_qt : it > i_begin;
+    if (mine && wave_active && !(CAUSAL && q_base + BQ - 1 < key0)) {
+      const uint8_t* Qs = stage(i);
       const uint8_t* dOs = Qs + TILE_B;
       const float* lse2s = (const float*)(Qs + 2 * TILE_B);
       const float* dvs = lse2s + BQ;
+      const uint8_t* X1 = role_a ? Qs : dOs;  // A operand of the first product (row reads)
+      const uint8_t* X2 = role_a ? dOs : Qs;  // B operand of the second (transposed reads)
+      uint8_t* xb = xbuf + ((i & 1) * 4 + pair) * (Cfg::XBUF_B / 4);
       const bool need_mask = (CAUSAL && key0 + 31 > q_base) || (q_base + BQ > N);
 #pragma unroll
       for (int qb = 0; qb < BQ / 32; ++qb) {
-        f32x16 s, dp;
+        f32x16 s;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          s[e] = 0.f;
-          dp[e] = 0.f;
-        }
+        for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {  // two independent chains, interleaved
-          const int addr = row_read_addr<D>(qb * 32 + lr, 2 * st + h);
-          const vec8 qa = *(const vec8*)(Qs + addr);
-          s = TR::mma(qa, kf[st], s);
-          if (DO_DK) {
-            const vec8 da = *(const vec8*)(dOs + addr);
-            dp = TR::mma(da, vf[st], dp);
-          }
+        for (int st = 0; st < D / 16; ++st) {
+          const vec8 xa = *(const vec8*)(X1 + row_read_addr<D>(qb * 32 + lr, 2 * st + h));
+          s = TR::mma(xa, xf[st], s);
         }
-        // keep the fragment reads one step ahead of the MFMAs that consume them
-        constexpr int PER = DO_DK ? 2 : 1;
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PER, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
         for (int st = 0; st < D / 16 - 2; ++st) {
-          __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * PER, 0);
-        // element 4j + r is query qb*32 + 8j + 4h + r of the tile, key = this lane's key; the
-        // exponent (in place in s) is the log2-domain logit minus the row's log2 LSE, -inf
-        // where masked (P = 0 there)
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        // element 4j + r: query q_base + qb*32 + 8j + 4h + r, this lane's key
+        u32x4* xq = (u32x4*)(xb + qb * 2048 + lane * 16);
+        vec8 pk[2];
+        if (role_a) {
+          float p[16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 l4 = *(const f32x4*)(lse2s + qb * 32 + 8 * j + 4 * h);
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 l4 = *(const f32x4*)(lse2s + qb * 32 + 8 * j + 4 * h);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) s[4 * j + r] = fmaf(s[4 * j + r], a.c, -l4[r]);
-        }
-        if (need_mask) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int qq = q_base + qb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-            s[e] = ((CAUSAL && key > qq) || qq >= N) ? -__builtin_inff() : s[e];
+            for (int r = 0; r < 4; ++r) p[4 * j + r] = fmaf(s[4 * j + r], a.c, -l4[r]);
           }
-        }
-        float p[16], ds[16];
+          if (need_mask) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
-          if (DO_DK) d4 = *(const f32x4*)(dvs + qb * 32 + 8 * j + 4 * h);
-          // keep bits of this lane's key for queries q_base + qb*32 + 8j + 4h + r, r = 0..3
-          uint32_t kbits = 0xFu;
-          if (DROP)
-            kbits = quad_keep_bits((uint32_t)key >> 2, (uint32_t)(q_base + qb * 32 + 8 * j + 4 * h), (uint32_t)bh,
-                                   a.drop, lane);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = 4 * j + r;
-            p[e] = __builtin_amdgcn_exp2f(s[e]);
-            if (DROP) {
-              const bool kept = (kbits >> r) & 1u;
-              if (DO_DK) ds[e] = p[e] * ((kept ? dp[e] * a.drop.inv_keep : 0.f) - d4[r]);
-              if (DO_DV) p[e] = kept ? p[e] * a.drop.inv_keep : 0.f;
-            } else {
-              ds[e] = p[e] * (dp[e] - d4[r]);
+            for (int e = 0; e < 16; ++e) {
+              const int qq = q_base + qb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+              p[e] = ((CAUSAL && key > qq) || qq >= N) ? -__builtin_inff() : p[e];
             }
           }
-        }
-        vec8 pp[2], dsp[2];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          u32x4 pu, du;
+          for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(p[e]);
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            pu[e2] = TR::pack2(p[8 * half + 2 * e2], p[8 * half + 2 * e2 + 1]);
-            du[e2] = TR::pack2(ds[8 * half + 2 * e2], ds[8 * half + 2 * e2 + 1]);
+          for (int half = 0; half < 2; ++half) {
+            u32x4 pu;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) pu[e2] = TR::pack2(p[8 * half + 2 * e2], p[8 * half + 2 * e2 + 1]);
+            xq[half * 64] = pu;  // P for B
+            if (DROP) {
+              const uint32_t kb = quad_keep_bits((uint32_t)key >> 2, (uint32_t)(q_base + qb * 32 + 8 * (2 * half) + 4 * h),
+                                                 (uint32_t)bh, a.drop, lane);
+              const uint32_t kb2 = quad_keep_bits((uint32_t)key >> 2,
+                                                  (uint32_t)(q_base + qb * 32 + 8 * (2 * half + 1) + 4 * h),
+                                                  (uint32_t)bh, a.drop, lane);
+              const uint32_t bits = kb | (kb2 << 4);
+#pragma unroll
+              for (int e2 = 0; e2 < 4; ++e2) {
+                const int e = 2 * e2;
+                const float x0 = ((bits >> e) & 1u) ? p[8 * half + e] * a.drop.inv_keep : 0.f;
+                const float x1 = ((bits >> (e + 1)) & 1u) ? p[8 * half + e + 1] * a.drop.inv_keep : 0.f;
+                pu[e2] = TR::pack2(x0, x1);
+              }
+            }
+            pk[half] = bitcast<vec8>(pu);
           }
-          pp[half] = bitcast<vec8>(pu);
-          dsp[half] = bitcast<vec8>(du);
+        } else {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const u32x4 pu = xq[half * 64];
+            uint32_t bits = 0xFFu;
+            if (DROP)
+              bits = quad_keep_bits((uint32_t)key >> 2, (uint32_t)(q_base + qb * 32 + 8 * (2 * half) + 4 * h),
+                                    (uint32_t)bh, a.drop, lane) |
+                     (quad_keep_bits((uint32_t)key >> 2, (uint32_t)(q_base + qb * 32 + 8 * (2 * half + 1) + 4 * h),
+                                     (uint32_t)bh, a.drop, lane)
+                      << 4);
+            u32x4 du;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+              const f32x4 d4 = *(const f32x4*)(dvs + qb * 32 + 8 * (2 * half + jj) + 4 * h);
+#pragma unroll
+              for (int r2 = 0; r2 < 2; ++r2) {
+                const int e = 8 * half + 4 * jj + 2 * r2;  // element index in s
+                float p0, p1;
+                unpack2<TR>(pu[2 * jj + r2], p0, p1);
+                float dp0 = s[e], dp1 = s[e + 1];
+                if (DROP) {
+                  const int bi = 4 * jj + 2 * r2;
+                  dp0 = ((bits >> bi) & 1u) ? dp0 * a.drop.inv_keep : 0.f;
+                  dp1 = ((bits >> (bi + 1)) & 1u) ? dp1 * a.drop.inv_keep : 0.f;
+                }
+                du[2 * jj + r2] = TR::pack2(p0 * (dp0 - d4[2 * r2]), p1 * (dp1 - d4[2 * r2 + 1]));
+              }
+            }
+            pk[half] = bitcast<vec8>(du);
+          }
         }
-        // dV += P^T dO and dK += dS^T Q over this block's two 16-query chunks; B operands via
-        // the transposed LDS read.
+        // dV += P^T dO (A) or dK += dS^T Q (B) over this block's two 16-query chunks
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int c = 2 * qb + half;
 #pragma unroll
           for (int b = 0; b < D / 32; ++b) {
-            const int a0 = tr_read_addr<D>(16 * c + tr_row, 32 * b + tr_col);
-            const int a1 = tr_read_addr<D>(16 * c + tr_row + 8, 32 * b + tr_col);
-            if (DO_DV) {
-              const i16x4 d0 = lds_read_tr16(dOs + a0);
-              const i16x4 d1 = lds_read_tr16(dOs + a1);
-              const i16x8 dd = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-              adv[b] = TR::mma(pp[half], bitcast<vec8>(dd), adv[b]);
-            }
-            if (DO_DK) {
-              const i16x4 q0 = lds_read_tr16(Qs + a0);
-              const i16x4 q1 = lds_read_tr16(Qs + a1);
-              const i16x8 qq = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-              adk[b] = TR::mma(dsp[half], bitcast<vec8>(qq), adk[b]);
-            }
+            const i16x4 x0 = lds_read_tr16(X2 + tr_read_addr<D>(16 * c + tr_row, 32 * b + tr_col));
+            const i16x4 x1 = lds_read_tr16(X2 + tr_read_addr<D>(16 * c + tr_row + 8, 32 * b + tr_col));
+            const i16x8 xx = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            acc[b] = TR::mma(pk[half], bitcast<vec8>(xx), acc[b]);
           }
         }
       }
     }
-    if (i + 1 < n_qt) store_rows(i + 1);
+    if (it + 1 < n_qt) store_rows(it + 1);
   }
 
   if (!wave_active) return;
-  // Output element 4j + r of block b is key key0 + 8j + 4h + r, column 32b + lr.
+  uint16_t* out = role_a ? a.dv : a.dk;
+  const float osc = role_a ? 1.f : a.scale;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -393,11 +412,8 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
       const int kk = key0 + 8 * j + 4 * h + r;
       if (kk < N) {
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b) {
-          const size_t idx = head + (size_t)kk * D + 32 * b + lr;
-          if (DO_DK) a.dk[idx] = __builtin_bit_cast(uint16_t, TR::from_f32(adk[b][4 * j + r] * a.scale));
-          if (DO_DV) a.dv[idx] = __builtin_bit_cast(uint16_t, TR::from_f32(adv[b][4 * j + r]));
-        }
+        for (int b = 0; b < D / 32; ++b)
+          out[head + (size_t)kk * D + 32 * b + lr] = __builtin_bit_cast(uint16_t, TR::from_f32(acc[b][4 * j + r] * osc));
       }
     }
 }
@@ -632,18 +648,12 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
   }
   const bool big = (size_t)r.N * D * 2 >= ((size_t)1 << 31);
   a.bh_total = (int)BH;
-  if (stage < 0 || stage == 1 || stage == 3 || stage == 4) {
-    a.ntiles = (r.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
-    dim3 g1((unsigned)(BH * a.ntiles));
-    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, g1, dim3(DkdvCfg<D>::NT), 0, st, a); };
-    const bool dv_pass = stage != 4, dk_pass = stage != 3;
-    if (r.causal) {
-      if (dv_pass) big ? go(bwd_dkdv_kernel<TR, D, true, true, 1, DROP>) : go(bwd_dkdv_kernel<TR, D, true, false, 1, DROP>);
-      if (dk_pass) big ? go(bwd_dkdv_kernel<TR, D, true, true, 2, DROP>) : go(bwd_dkdv_kernel<TR, D, true, false, 2, DROP>);
-    } else {
-      if (dv_pass) big ? go(bwd_dkdv_kernel<TR, D, false, true, 1, DROP>) : go(bwd_dkdv_kernel<TR, D, false, false, 1, DROP>);
-      if (dk_pass) big ? go(bwd_dkdv_kernel<TR, D, false, true, 2, DROP>) : go(bwd_dkdv_kernel<TR, D, false, false, 2, DROP>);
-    }
+  if (stage < 0 || stage == 1) {
+    a.ntiles = (r.N + PairCfg<D>::BKV - 1) / PairCfg<D>::BKV;
+    dim3 gp((unsigned)(BH * a.ntiles));
+    auto gop = [&](auto kern) { hipLaunchKernelGGL(kern, gp, dim3(PairCfg<D>::NT), 0, st, a); };
+    if (r.causal) big ? gop(bwd_dkdv_pair_kernel<TR, D, true, true, DROP>) : gop(bwd_dkdv_pair_kernel<TR, D, true, false, DROP>);
+    else big ? gop(bwd_dkdv_pair_kernel<TR, D, false, true, DROP>) : gop(bwd_dkdv_pair_kernel<TR, D, false, false, DROP>);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -50,8 +50,7 @@ bool fwd_tile_supported(int dtype, int d, int Br, int Bc);
 hipError_t launch_fwd(const FwdReq& r, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
-// stage: 0 = preprocess, 1 = dK/dV (dV pass then dK pass), 2 = dQ, 3 = dV pass only,
-// 4 = dK pass only; -1 = preprocess, dK/dV, dQ in order
+// stage: 0 = preprocess, 1 = dK/dV, 2 = dQ; -1 = preprocess, dK/dV, dQ in order
 hipError_t launch_bwd(const BwdReq& r, hipStream_t stream, int stage = -1);
 
 // Split-KV forward (query rows Nq against Nk keys, the keys cut into num_splits ranges).

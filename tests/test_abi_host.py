@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
     names = _declared()
     assert {"fattn_fwd", "fattn_fwd_tiled", "fattn_bwd", "fattn_bwd_workspace_size",
             "fattn_strerror", "fattn_version", "fattn_bwd_preprocess", "fattn_bwd_dkdv",
-            "fattn_bwd_dv", "fattn_bwd_dk", "fattn_bwd_dq", "fattn_fwd_splitkv",
+            "fattn_bwd_dq", "fattn_fwd_splitkv",
             "fattn_fwd_splitkv_workspace_size", "fattn_splitkv_num_splits", "fattn_fwd_partial",
             "fattn_combine", "fattn_fwd_kouter", "fattn_fwd_kouter_workspace_size",
             "fattn_fwd_dropout", "fattn_bwd_dropout", "fattn_fwd_blocksparse"} <= set(names)
@@ -135,12 +135,11 @@ def test_binding_refuses_host_tensors():
     (lambda: fa.fattn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], P[5], 1, 1, 8, 64, 0.1, 0, 2), -11),
     (lambda: fa.fattn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], MIS, 1, 1, 8, 64, 0.1, 0, 2), -6),
     (lambda: fa.fattn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 0, 1, 8, 64, 0.1, 0, 2), -2),
-    (lambda: fa.fattn_bwd_dv(P[0], P[1], P[2], P[3], P[4], P[5], None, 1, 1, 8, 64, 0.1, 0, 2), -1),
-    (lambda: fa.fattn_bwd_dv(P[0], P[1], P[2], P[3], P[4], P[5], P[3], 1, 1, 8, 64, 0.1, 0, 2), -11),
-    (lambda: fa.fattn_bwd_dv(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 1, 1, 8, 96, 0.1, 0, 2), -3),
-    (lambda: fa.fattn_bwd_dk(P[0], P[1], P[2], P[3], P[4], P[5], MIS, 1, 1, 8, 64, 0.1, 0, 2), -6),
-    (lambda: fa.fattn_bwd_dk(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 1, 1, 8, 64, 0.1, 2, 2), -12),
-    (lambda: fa.fattn_bwd_dk(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 1, 1, 8, 64, 0.1, 0, 0), -4),
+    (lambda: fa.fattn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], None, 1, 1, 8, 64, 0.1, 0, 2), -1),
+    (lambda: fa.fattn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], P[3], 1, 1, 8, 64, 0.1, 0, 2), -11),
+    (lambda: fa.fattn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 1, 1, 8, 96, 0.1, 0, 2), -3),
+    (lambda: fa.fattn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 1, 1, 8, 64, 0.1, 2, 2), -12),
+    (lambda: fa.fattn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 1, 1, 8, 64, 0.1, 0, 0), -4),
 ])
 def test_backward_stages_reject_bad_arguments(L, call, status):
     assert call() == status
