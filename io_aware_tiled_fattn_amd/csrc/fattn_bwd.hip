@@ -303,13 +303,9 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
           const vec8 xa = *(const vec8*)(X1 + row_read_addr<D>(qb * 32 + lr, 2 * st + h));
           s = TR::mma(xa, xf[st], s);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int st = 0; st < D / 16 - 2; ++st) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        // all fragment reads first, so their latency hides behind the MFMA chain
+        __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
         // element 4j + r: query q_base + qb*32 + 8j + 4h + r, this lane's key
         u32x4* xq = (u32x4*)(xb + qb * 2048 + lane * 16);
         vec8 pk[2];
@@ -397,6 +393,9 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
             acc[b] = TR::mma(pk[half], bitcast<vec8>(xx), acc[b]);
           }
         }
+        // likewise: the transposed reads of both chunks, then their MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * 2 * (D / 32), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 32), 0);
       }
     }
     if (it + 1 < n_qt) store_rows(it + 1);
@@ -546,7 +545,7 @@ __global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)
       }
       const int row = kb * 32 + lr;
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) {  // two independent chains, interleaved
+      for (int st = 0; st < D / 16; ++st) {  // two independent chains
         const vec8 ka = *(const vec8*)(Ks + row_read_addr<D>(row, 2 * st + h));
         const vec8 va = *(const vec8*)(Vs + row * (D * 2) + (((2 * st + h) ^ swz_rowread<D>(row)) << 4));
         s = TR::mma(ka, qf[st], s);
