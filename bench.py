@@ -101,6 +101,7 @@ def cpu_oracle_baseline(budget_s: float = 20.0):
 
 
 SWEEP_N = (1024, 2048, 4096, 8192, 16384)
+FWD_TILES = ((64, 64), (64, 128), (128, 64), (128, 128), (256, 64), (256, 128))
 
 
 def n_sweep(torch, fa):
@@ -251,9 +252,20 @@ def main(argv=None):
     ms_drop_fwd = T(lambda: fa.forward(q, k, v, causal=True, out=o, lse=lse, p_drop=p_drop, seed=seed))
     ms_drop_bwd = T(lambda: fa.backward(q, k, v, o, do, lse, causal=True, workspace=ws, p_drop=p_drop, seed=seed))
 
-    # Prefill-shaped forward (B=4).
+    # Prefill-shaped forward (B=4), default tile, then every tile the d = 128 forward supports.
     ms_fwd3 = T(lambda: fa.forward(q3, k3, v3, causal=True, out=o3, lse=l3))
+    tile_ms = {}
+    for br, bc in FWD_TILES:
+        tile_ms[(br, bc)] = T(lambda: fa.forward(q3, k3, v3, causal=True, Br=br, Bc=bc, out=o3, lse=l3))
     del q3, k3, v3, o3, l3
+
+    # Long-context forward (B=1 H=32 N=16384 d=128), both masks.
+    inp4 = fi.workload_inputs(4)
+    q4, k4, v4, _ = _upload(inp4, torch)
+    del inp4
+    o4, l4 = torch.empty_like(q4), torch.empty(q4.shape[:3], dtype=torch.float32, device="cuda")
+    ms_fwd4 = {c: T(lambda: fa.forward(q4, k4, v4, causal=c, out=o4, lse=l4)) for c in (True, False)}
+    del q4, k4, v4, o4, l4
 
     tr_all = profiling.load_traffic(os.path.join(ROOT, "profiles"))
 
@@ -332,7 +344,8 @@ def main(argv=None):
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "ms_per_launch": round(ms[dom], 4), "algorithmic_tflop_per_launch": round(fl / 1e12, 4)}
 
-    fwd3_tf = tf(flops_fwd(w3.B, w3.H, w3.N, w3.d, True), ms_fwd3)
+    f3 = flops_fwd(w3.B, w3.H, w3.N, w3.d, True)
+    fwd3_tf = tf(f3, ms_fwd3)
     bwd_tf = tf(2.5 * f_fwd, ms["bwd"])
     result = {
         "metric": "attention fwd/bwd TFLOP/s and % of MI355X bf16 MFMA peak at N=4096, d=128",
@@ -351,9 +364,18 @@ def main(argv=None):
                    "B": B, "H": H, "N": N, "d": d, "causal": True},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd": {"workload": "B=4 H=16 N=4096 d=128 causal", "ms": round(ms_fwd3, 4),
-                "tflops": round(fwd3_tf, 1), "frac_of_peak": round(fwd3_tf / PEAK_BF16_TFLOPS, 4)},
+                "tflops": round(fwd3_tf, 1), "frac_of_peak": round(fwd3_tf / PEAK_BF16_TFLOPS, 4),
+                "tile_default": "256x128",
+                "tiles": {f"{br}x{bc}": {"ms": round(t_, 4), "tflops": round(tf(f3, t_), 1)}
+                          for (br, bc), t_ in tile_ms.items()}},
+        "fwd_long": {f"{'causal' if c else 'noncausal'}": {
+                         "workload": f"B=1 H=32 N=16384 d=128 {'causal' if c else 'non-causal'}",
+                         "ms": round(t_, 4), "tflops": round(tf(flops_fwd(1, 32, 16384, 128, c), t_), 1),
+                         "frac_of_peak": round(tf(flops_fwd(1, 32, 16384, 128, c), t_) / PEAK_BF16_TFLOPS, 4)}
+                     for c, t_ in ms_fwd4.items()},
         "bwd": {"workload": "B=2 H=16 N=4096 d=128 causal", "ms": round(ms["bwd"], 4),
-                "tflops": round(bwd_tf, 1), "frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)},
+                "tflops": round(bwd_tf, 1), "frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                "workspace_bytes": ws.numel()},
         "kernel_ms": {k_: round(t, 4) for k_, t in ms.items()},
         "roofline": roof,
     }

@@ -1,4 +1,5 @@
-"""Build libfattn.so for gfx950 with hipcc (no GPU needed: hipcc cross-compiles).
+"""Build libfattn.so (and the issue-rate micro-benchmark) for gfx950 with hipcc (no GPU needed:
+hipcc cross-compiles).
 
 Usage: python -m io_aware_tiled_fattn_amd.build [--verbose] [--resource-usage]
 """
@@ -52,6 +53,19 @@ def _compile(src, hipcc, extra, verbose):
     return obj, text
 
 
+TOOLS = {"issue_rates.hip": os.path.join(HERE, "issue_rates")}  # stand-alone measurement programs
+
+
+def _build_tool(src, exe, hipcc, verbose):
+    cmd = [hipcc, *[c for c in COMMON if c != "-fPIC"], os.path.join(CSRC, src), "-o", exe + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}{r.stderr}")
+    os.replace(exe + ".tmp", exe)
+
+
 def build(verbose: bool = False, resource_usage: bool = False) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -67,6 +81,8 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, OUT)
+    for src, exe in TOOLS.items():
+        _build_tool(src, exe, hipcc, verbose)
     return OUT
 
 
