@@ -239,6 +239,8 @@ def main(argv=None):
     bmask_np = fi.block_mask(B, H, nbk, 0.25, 5)
     bmask = torch.from_numpy(bmask_np).cuda()
     ms_bs = T(lambda: fa.forward_blocksparse(q, k, v, bmask, causal=True, out=o, lse=lse))
+    # and its backward (on the block-sparse forward's O and LSE)
+    ms_bs_bwd = T(lambda: fa.backward_blocksparse(q, k, v, o, do, lse, bmask, causal=True, workspace=ws))
     # allowed (query, key) pairs: full blocks below the diagonal, half (with the diagonal) on it
     tri = np.tril(np.ones((nbk, nbk), bool), -1)
     pairs_bs = float((bmask_np.astype(bool) & tri).sum() * 128 * 128
@@ -398,7 +400,10 @@ def main(argv=None):
                                          "plus the diagonal",
                              "ms": round(ms_bs, 4), "allowed_fraction_of_causal_pairs": round(density, 4),
                              "tflops_on_allowed_pairs": round(tf(f_bs, ms_bs), 1),
-                             "time_vs_dense": round(ms_bs / ms["fwd"], 3)}
+                             "time_vs_dense": round(ms_bs / ms["fwd"], 3),
+                             "bwd_ms": round(ms_bs_bwd, 4),
+                             "bwd_tflops_on_allowed_pairs": round(tf(2.5 * f_bs, ms_bs_bwd), 1),
+                             "bwd_time_vs_dense": round(ms_bs_bwd / ms["bwd"], 3)}
     result["dropout"] = {"workload": "B=2 H=16 N=4096 d=128 causal, p = 0.1 (Philox4x32-10 keep mask)",
                          "fwd_ms": round(ms_drop_fwd, 4), "bwd_ms": round(ms_drop_bwd, 4),
                          "fwd_tflops": round(tf(f_fwd, ms_drop_fwd), 1),

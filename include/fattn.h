@@ -146,6 +146,22 @@ int fattn_bwd_dropout(const void* q, const void* k, const void* v, const void* o
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward of fattn_fwd_blocksparse (same block_mask, layout [B, H, nb, nb] uint8 on the device):
+ * the chain rule through the block-restricted definition. Masked scores carry P = 0, so
+ * dV = P^T dO, dP = dO V^T, D = rowsum(dO * O), dS = P * (dP - D), dQ = scale dS K,
+ * dK = scale dS^T Q; a row with no allowed key (LSE = -inf) gets dQ = 0 and adds nothing to dK, dV.
+ * Only (query, key) tiles whose mask block is set are read and computed: the dK/dV kernel visits
+ * the query tiles of its key block's mask column, the dQ kernel the key tiles of its two mask
+ * rows. Same buffers and checks as fattn_bwd, plus block_mask non-null (FATTN_ERR_NULL) and
+ * distinct from the outputs and the workspace (FATTN_ERR_ALIAS). Not combinable with dropout.
+ */
+int fattn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                          const float* lse, void* dq, void* dk, void* dv,
+                          int B, int H, int N, int d, float scale, int causal, int dtype,
+                          const unsigned char* block_mask, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
  * The three stages of fattn_bwd, in the order fattn_bwd enqueues them, for callers that want to
  * schedule or time them separately. Same conventions and checks as fattn_bwd; `dvec` is the
  * float32 [B,H,N] row vector D = rowsum(dO * O) (the first bytes of fattn_bwd's workspace).

@@ -9,7 +9,7 @@ Low-level names mirror the C entry points (``fattn_fwd``, ``fattn_fwd_tiled``, `
 ``fattn_fwd_splitkv``, ``fattn_fwd_splitkv_workspace_size``,
 ``fattn_splitkv_num_splits``, ``fattn_fwd_partial``, ``fattn_combine``, ``fattn_fwd_kouter``,
 ``fattn_fwd_kouter_workspace_size``, ``fattn_fwd_dropout``, ``fattn_bwd_dropout``,
-``fattn_fwd_blocksparse``,
+``fattn_fwd_blocksparse``, ``fattn_bwd_blocksparse``,
 ``fattn_strerror``, ``fattn_version``) and take raw device addresses. ``forward``, ``backward``,
 ``backward_stages``, ``forward_splitkv``, ``forward_partial``, ``combine`` and ``forward_kouter`` wrap them for
 contiguous torch tensors.
@@ -29,6 +29,7 @@ __all__ = [
     "fattn_fwd_partial", "fattn_combine", "forward_splitkv", "forward_partial", "combine",
     "fattn_fwd_kouter", "fattn_fwd_kouter_workspace_size", "forward_kouter",
     "fattn_fwd_dropout", "fattn_bwd_dropout", "fattn_fwd_blocksparse", "forward_blocksparse",
+    "fattn_bwd_blocksparse", "backward_blocksparse",
 ]
 
 FATTN_F32, FATTN_F16, FATTN_BF16 = 0, 1, 2
@@ -93,6 +94,8 @@ def lib():
     L.fattn_bwd_dropout.restype = i
     L.fattn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, vp]
     L.fattn_fwd_blocksparse.restype = i
+    L.fattn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, vp, sz, vp]
+    L.fattn_bwd_blocksparse.restype = i
     L.fattn_strerror.argtypes = [i]
     L.fattn_strerror.restype = ctypes.c_char_p
     L.fattn_version.argtypes = []
@@ -180,6 +183,12 @@ def fattn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal
 
 def fattn_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, block_mask, stream=None) -> int:
     return lib().fattn_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, block_mask, stream)
+
+
+def fattn_bwd_blocksparse(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, block_mask,
+                          workspace, workspace_bytes, stream=None) -> int:
+    return lib().fattn_bwd_blocksparse(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype,
+                                       block_mask, workspace, workspace_bytes, stream)
 
 
 def fattn_strerror(status: int) -> str:
@@ -452,3 +461,29 @@ def forward_blocksparse(q, k, v, block_mask, causal=False, scale=None, out=None,
     if st != 0:
         raise FattnError(st, "fattn_fwd_blocksparse")
     return out, lse
+
+
+def backward_blocksparse(q, k, v, o, do, lse, block_mask, causal=False, scale=None, workspace=None,
+                         stream=None):
+    """dQ, dK, dV of block-sparse attention (the same ``block_mask`` as forward_blocksparse)."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, q if n != "q" else None)
+    B, H, N, d = q.shape
+    nb = (N + 127) // 128
+    _check_dev(block_mask, "block_mask", (B, H, nb, nb), torch.uint8)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = dtype_code(q)
+    need = fattn_bwd_workspace_size(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = fattn_bwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                               lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                               B, H, N, d, float(scale), int(bool(causal)), code, block_mask.data_ptr(),
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               _stream(stream))
+    if st != 0:
+        raise FattnError(st, "fattn_bwd_blocksparse")
+    return dq, dk, dv

@@ -188,33 +188,58 @@ size_t fattn_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
   return fattn::bwd_workspace_bytes(B, H, N, d);
 }
 
-int fattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
-              const float* lse, void* dq, void* dk, void* dv,
-              int B, int H, int N, int d, float scale, int causal, int dtype,
-              void* workspace, size_t workspace_bytes, void* stream) {
+// Argument checks shared by the full backward entry points (extra: one more input, may be null).
+static int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                     float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                     const void* extra) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FATTN_ERR_NULL;
   int st = check_common(B, H, N, d, dtype);
   if (st != FATTN_OK) return st;
   if (dtype == FATTN_F32) return FATTN_ERR_DTYPE;
   if (causal != 0 && causal != 1) return FATTN_ERR_CAUSAL;
   if (!std::isfinite(scale)) return FATTN_ERR_SCALE;
-  const void* ins[6] = {q, k, v, o, dO, lse};
+  const void* ins[7] = {q, k, v, o, dO, lse, extra};
   void* outs[3] = {dq, dk, dv};
-  for (const void* p : ins)
-    if (!aligned16(p)) return FATTN_ERR_ALIGN;
+  for (int i = 0; i < 6; ++i)
+    if (!aligned16(ins[i])) return FATTN_ERR_ALIGN;
   for (void* p : outs)
     if (!aligned16(p)) return FATTN_ERR_ALIGN;
   for (void* p : outs)
-    for (const void* s : ins)
-      if (p == s) return FATTN_ERR_ALIAS;
+    for (const void* s2 : ins)
+      if (s2 && p == s2) return FATTN_ERR_ALIAS;
   if (dq == dk || dq == dv || dk == dv) return FATTN_ERR_ALIAS;
   const size_t need = fattn::bwd_workspace_bytes(B, H, N, d);
   if (!workspace || workspace_bytes < need) return FATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FATTN_ERR_ALIGN;
   for (void* p : outs)
     if (p == workspace) return FATTN_ERR_ALIAS;
-  for (const void* s : ins)
-    if (s == workspace) return FATTN_ERR_ALIAS;
+  for (const void* s2 : ins)
+    if (s2 == workspace) return FATTN_ERR_ALIAS;
+  return FATTN_OK;
+}
+
+int fattn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                          const float* lse, void* dq, void* dk, void* dv,
+                          int B, int H, int N, int d, float scale, int causal, int dtype,
+                          const unsigned char* block_mask, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (!block_mask) return FATTN_ERR_NULL;
+  int st = check_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, workspace,
+                     workspace_bytes, block_mask);
+  if (st != FATTN_OK) return st;
+  fattn::BwdReq r{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, (float*)workspace};
+  r.bmask = block_mask;
+  return launch_status(fattn::launch_bwd(r, (hipStream_t)stream));
+}
+
+int fattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+              const float* lse, void* dq, void* dk, void* dv,
+              int B, int H, int N, int d, float scale, int causal, int dtype,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, workspace,
+                     workspace_bytes, nullptr);
+  if (st != FATTN_OK) return st;
   fattn::BwdReq r{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, (float*)workspace};
   return launch_status(fattn::launch_bwd(r, (hipStream_t)stream));
 }
@@ -228,29 +253,9 @@ int fattn_bwd_dropout(const void* q, const void* k, const void* v, const void* o
   if (p_drop == 0.f)
     return fattn_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, workspace,
                      workspace_bytes, stream);
-  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FATTN_ERR_NULL;
-  int st = check_common(B, H, N, d, dtype);
+  int st = check_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, workspace,
+                     workspace_bytes, nullptr);
   if (st != FATTN_OK) return st;
-  if (dtype == FATTN_F32) return FATTN_ERR_DTYPE;
-  if (causal != 0 && causal != 1) return FATTN_ERR_CAUSAL;
-  if (!std::isfinite(scale)) return FATTN_ERR_SCALE;
-  const void* ins[6] = {q, k, v, o, dO, lse};
-  void* outs[3] = {dq, dk, dv};
-  for (const void* p : ins)
-    if (!aligned16(p)) return FATTN_ERR_ALIGN;
-  for (void* p : outs)
-    if (!aligned16(p)) return FATTN_ERR_ALIGN;
-  for (void* p : outs)
-    for (const void* s2 : ins)
-      if (p == s2) return FATTN_ERR_ALIAS;
-  if (dq == dk || dq == dv || dk == dv) return FATTN_ERR_ALIAS;
-  const size_t need = fattn::bwd_workspace_bytes(B, H, N, d);
-  if (!workspace || workspace_bytes < need) return FATTN_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return FATTN_ERR_ALIGN;
-  for (void* p : outs)
-    if (p == workspace) return FATTN_ERR_ALIAS;
-  for (const void* s2 : ins)
-    if (s2 == workspace) return FATTN_ERR_ALIAS;
   fattn::BwdReq r{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, (float*)workspace};
   r.dropout = true;
   r.drop = drop_params(p_drop, seed);

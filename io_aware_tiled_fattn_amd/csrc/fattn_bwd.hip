@@ -48,6 +48,8 @@ struct BwdArgs {
   float c;      // scale * log2(e) (signed)
   float scale;  // signed softmax scale
   DropParams drop;  // dropout on P (DROP instances only)
+  const uint8_t* bmask;  // block mask [B*H][nb][nb] over 128 x 128 (query, key) blocks (SPARSE)
+  int nb;                // ceil(N / 128)
 };
 
 template <typename TR>
@@ -167,7 +169,9 @@ __device__ inline void unpack2<F16>(uint32_t u, float& x, float& y) {
   y = f[1];
 }
 
-template <typename TR, int D, bool CAUSAL, bool BIG, bool DROP>
+// SPARSE: block-sparse attention over 128 x 128 (query, key) blocks; the work-group's 128 keys are
+// one mask column, and only the query tiles whose mask block is set are loaded and computed.
+template <typename TR, int D, bool CAUSAL, bool BIG, bool DROP, bool SPARSE>
 __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_pair_kernel(BwdArgs a) {
   using Cfg = PairCfg<D>;
   using vec8 = typename TR::vec8;
@@ -227,9 +231,12 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
   const uint32_t head_bytes = BIG ? 0u : (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Qh, head_bytes);
   const __amdgpu_buffer_rsrc_t rdO = make_rsrc(dOh, head_bytes);
-  auto stage = [&](int i) { return smem + (i % NSTG) * Cfg::STAGE_B; };
-  auto issue = [&](int i) {
-    uint8_t* st = stage(i) + w * 64 * 16;
+  // tiles are numbered by their position in the sequence the work-group visits (consecutive
+  // tiles, or the allowed ones of a block-sparse run): position p sits in stage p % 3 and its P in
+  // exchange buffer p % 2
+  auto stage = [&](int p) { return smem + (p % NSTG) * Cfg::STAGE_B; };
+  auto issue = [&](int i, int p) {
+    uint8_t* st = stage(p) + w * 64 * 16;
     if (!BIG && (i + 1) * BQ <= N) {
       const uint32_t soff = (uint32_t)(i * BQ) * (D * 2);
 #pragma unroll
@@ -257,9 +264,9 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
       dvr = a.dvec[rowbase + q];
     }
   };
-  auto store_rows = [&](int i) {
+  auto store_rows = [&](int p) {
     if (tid < BQ) {
-      float* rows = (float*)(stage(i) + 2 * TILE_B);
+      float* rows = (float*)(stage(p) + 2 * TILE_B);
       rows[tid] = lr2;
       rows[BQ + tid] = dvr;
     }
@@ -268,30 +275,45 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  if (i_begin < n_qt) {
-    load_rows(i_begin);
-    issue(i_begin);
-    store_rows(i_begin);
+  // query tile i's mask block: row (i BQ) / 128, column jt (BKV = 128)
+  const uint8_t* bcol = SPARSE ? a.bmask + (size_t)bh * a.nb * a.nb + jt : nullptr;
+  auto next = [&](int i) {
+    ++i;
+    if (SPARSE)
+      while (i < n_qt && bcol[(size_t)((i * BQ) >> 7) * a.nb] == 0) ++i;
+    return i;
+  };
+  // A dense run visits the tiles i_begin, i_begin + 1, ...; a block-sparse run only the allowed
+  // ones. Either way the visited tiles take positions 0, 1, ...
+  int cur = SPARSE ? next(i_begin - 1) : i_begin;  // A's tile
+  int prev = -1;                                   // B's tile (A's previous one)
+  if (cur < n_qt) {
+    load_rows(cur);
+    issue(cur, 0);
+    store_rows(0);
   }
-  // iteration it: A runs tile it, B runs tile it - 1; the last iteration is B's alone
-  for (int it = i_begin; it <= n_qt; ++it) {
+  // iteration p: A runs the tile at position p, B the one at p - 1; the last iteration is B's.
+  // A dense run counts p over the tile indices i_begin .. n_qt.
+  for (int p = 0; cur < n_qt || prev >= 0; ++p) {
     wait_vmcnt<0>();
     barrier_lds();
-    if (it + 1 < n_qt) {
-      load_rows(it + 1);
-      issue(it + 1);
+    const int nxt = cur < n_qt ? next(cur) : n_qt;
+    if (nxt < n_qt) {
+      load_rows(nxt);
+      issue(nxt, p + 1);
     }
-    const int i = role_a ? it : it - 1;
+    const int i = role_a ? cur : prev;
+    const int pos = role_a ? p : p - 1;
     const int q_base = i * BQ;
-    const bool mine = role_a ? it < n_qt : it > i_begin;
+    const bool mine = role_a ? cur < n_qt : prev >= 0;
     if (mine && wave_active && !(CAUSAL && q_base + BQ - 1 < key0)) {
-      const uint8_t* Qs = stage(i);
+      const uint8_t* Qs = stage(pos);
       const uint8_t* dOs = Qs + TILE_B;
       const float* lse2s = (const float*)(Qs + 2 * TILE_B);
       const float* dvs = lse2s + BQ;
       const uint8_t* X1 = role_a ? Qs : dOs;  // A operand of the first product (row reads)
       const uint8_t* X2 = role_a ? dOs : Qs;  // B operand of the second (transposed reads)
-      uint8_t* xb = xbuf + ((i & 1) * 4 + pair) * (Cfg::XBUF_B / 4);
+      uint8_t* xb = xbuf + ((pos & 1) * 4 + pair) * (Cfg::XBUF_B / 4);
       const bool need_mask = (CAUSAL && key0 + 31 > q_base) || (q_base + BQ > N);
 #pragma unroll
       for (int qb = 0; qb < BQ / 32; ++qb) {
@@ -398,7 +420,9 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 32), 0);
       }
     }
-    if (it + 1 < n_qt) store_rows(it + 1);
+    if (nxt < n_qt) store_rows(p + 1);
+    prev = cur < n_qt ? cur : -1;
+    cur = nxt;
   }
 
   if (!wave_active) return;
@@ -438,7 +462,10 @@ struct DqCfg {
 };
 
 // DROP: dS = P (dO V^T M / (1 - p) - D).
-template <typename TR, int D, bool CAUSAL, bool BIG, bool DROP>
+// SPARSE: block-sparse attention over 128 x 128 (query, key) blocks: the work-group loads the key
+// tiles whose mask column is set for either of its two mask rows, and each wave computes the ones
+// its own mask row allows.
+template <typename TR, int D, bool CAUSAL, bool BIG, bool DROP, bool SPARSE>
 __global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BwdArgs a) {
   using Cfg = DqCfg<D>;
   using vec8 = typename TR::vec8;
@@ -501,8 +528,9 @@ __global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)
   const uint32_t head_bytes = BIG ? 0u : (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rK = make_rsrc(Kh, head_bytes);
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(Vh, head_bytes);
-  auto issue = [&](int j) {
-    uint8_t* st = smem + (j & 1) * Cfg::STAGE_B + w * 64 * 16;
+  // key tile j into stage t & 1 (t = j except for block-sparse runs, which skip tiles)
+  auto issue = [&](int j, int t) {
+    uint8_t* st = smem + (t & 1) * Cfg::STAGE_B + w * 64 * 16;
     if (!BIG && (j + 1) * BK <= N) {
       const uint32_t soff = (uint32_t)(j * BK) * (D * 2);
 #pragma unroll
@@ -525,14 +553,34 @@ __global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  issue(0);
-  for (int j = 0; j < n_kv; ++j) {
+  // mask rows of this work-group and of this wave; key tile j lies in mask column (j BK) / 128
+  const uint8_t* bm = SPARSE ? a.bmask + (size_t)bh * a.nb * a.nb : nullptr;
+  const int r_lo = q_base >> 7, r_hi = min(a.nb, (q_base + BQ + 127) >> 7);
+  const int wave_row = min(q0, N - 1) >> 7;
+  auto next = [&](int j) {
+    ++j;
+    if (SPARSE)
+      while (j < n_kv) {
+        bool on = false;
+        for (int r = r_lo; r < r_hi; ++r) on = on || bm[(size_t)r * a.nb + ((j * BK) >> 7)] != 0;
+        if (on) break;
+        ++j;
+      }
+    return j;
+  };
+  int j = next(-1);
+  if (j < n_kv) issue(j, 0);
+  for (int t = 0; j < n_kv; ++t) {
     wait_vmcnt<0>();
     barrier_lds();
-    if (j + 1 < n_kv) issue(j + 1);
+    const int jn = next(j);
+    if (jn < n_kv) issue(jn, t + 1);
     const int k0 = j * BK;
+    const int jc = j;
+    j = jn;
     if (!(wave_active && k0 < wave_kv_end)) continue;
-    const uint8_t* Ks = smem + (j & 1) * Cfg::STAGE_B;
+    if (SPARSE && bm[(size_t)wave_row * a.nb + ((jc * BK) >> 7)] == 0) continue;
+    const uint8_t* Ks = smem + (t & 1) * Cfg::STAGE_B;
     const uint8_t* Vs = Ks + TILE_B;
     const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > q0);
 #pragma unroll
@@ -617,7 +665,7 @@ __global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)
 
 // ---------------------------------------------------------------------------------------------
 
-template <typename TR, int D, bool DROP>
+template <typename TR, int D, bool DROP, bool SPARSE>
 hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
   BwdArgs a;
   a.q = (const uint16_t*)r.q;
@@ -634,6 +682,8 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
   a.c = r.scale * kLog2e;
   a.scale = r.scale;
   a.drop = r.drop;
+  a.bmask = r.bmask;
+  a.nb = (r.N + 127) / 128;
   const long long BH = (long long)r.B * r.H;
   const long long rows = BH * r.N;
 
@@ -651,8 +701,10 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
     a.ntiles = (r.N + PairCfg<D>::BKV - 1) / PairCfg<D>::BKV;
     dim3 gp((unsigned)(BH * a.ntiles));
     auto gop = [&](auto kern) { hipLaunchKernelGGL(kern, gp, dim3(PairCfg<D>::NT), 0, st, a); };
-    if (r.causal) big ? gop(bwd_dkdv_pair_kernel<TR, D, true, true, DROP>) : gop(bwd_dkdv_pair_kernel<TR, D, true, false, DROP>);
-    else big ? gop(bwd_dkdv_pair_kernel<TR, D, false, true, DROP>) : gop(bwd_dkdv_pair_kernel<TR, D, false, false, DROP>);
+    if (r.causal)
+      big ? gop(bwd_dkdv_pair_kernel<TR, D, true, true, DROP, SPARSE>) : gop(bwd_dkdv_pair_kernel<TR, D, true, false, DROP, SPARSE>);
+    else
+      big ? gop(bwd_dkdv_pair_kernel<TR, D, false, true, DROP, SPARSE>) : gop(bwd_dkdv_pair_kernel<TR, D, false, false, DROP, SPARSE>);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -660,11 +712,11 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
     a.ntiles = (r.N + DqCfg<D>::BQ - 1) / DqCfg<D>::BQ;
     dim3 g2((unsigned)(BH * a.ntiles));
     if (r.causal) {
-      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, true, DROP>), g2, dim3(DqCfg<D>::NT), 0, st, a);
-      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, false, DROP>), g2, dim3(DqCfg<D>::NT), 0, st, a);
+      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, true, DROP, SPARSE>), g2, dim3(DqCfg<D>::NT), 0, st, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, false, DROP, SPARSE>), g2, dim3(DqCfg<D>::NT), 0, st, a);
     } else {
-      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, true, DROP>), g2, dim3(DqCfg<D>::NT), 0, st, a);
-      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, false, DROP>), g2, dim3(DqCfg<D>::NT), 0, st, a);
+      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, true, DROP, SPARSE>), g2, dim3(DqCfg<D>::NT), 0, st, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, false, DROP, SPARSE>), g2, dim3(DqCfg<D>::NT), 0, st, a);
     }
     e = hipGetLastError();
   }
@@ -679,17 +731,19 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   return (dvec + 255) & ~(size_t)255;
 }
 
-template <bool DROP>
+template <bool DROP, bool SPARSE>
 hipError_t launch_bwd_t(const BwdReq& r, hipStream_t st, int stage) {
   if (r.dtype == FATTN_BF16)
-    return r.d == 64 ? launch_all<Bf16, 64, DROP>(r, st, stage) : launch_all<Bf16, 128, DROP>(r, st, stage);
+    return r.d == 64 ? launch_all<Bf16, 64, DROP, SPARSE>(r, st, stage) : launch_all<Bf16, 128, DROP, SPARSE>(r, st, stage);
   if (r.dtype == FATTN_F16)
-    return r.d == 64 ? launch_all<F16, 64, DROP>(r, st, stage) : launch_all<F16, 128, DROP>(r, st, stage);
+    return r.d == 64 ? launch_all<F16, 64, DROP, SPARSE>(r, st, stage) : launch_all<F16, 128, DROP, SPARSE>(r, st, stage);
   return hipErrorInvalidValue;
 }
 
+// Dropout and block-sparse runs are separate instances; the two together are not built.
 hipError_t launch_bwd(const BwdReq& r, hipStream_t st, int stage) {
-  return r.dropout ? launch_bwd_t<true>(r, st, stage) : launch_bwd_t<false>(r, st, stage);
+  if (r.bmask) return r.dropout ? hipErrorInvalidValue : launch_bwd_t<false, true>(r, st, stage);
+  return r.dropout ? launch_bwd_t<true, false>(r, st, stage) : launch_bwd_t<false, false>(r, st, stage);
 }
 
 }  // namespace fattn

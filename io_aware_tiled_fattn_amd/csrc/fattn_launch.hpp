@@ -41,6 +41,7 @@ struct BwdReq {
   float* dvec;  // workspace: D = rowsum(dO * O), float32 [B, H, N]
   bool dropout = false;
   DropParams drop = {0u, 0u, 0u, 1.0f};
+  const uint8_t* bmask = nullptr;  // block-sparse backward: [B*H][nb][nb] mask over 128 x 128 blocks
 };
 
 // Default forward tile for (dtype, d, causal): returns false if none exists.

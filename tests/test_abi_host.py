@@ -37,7 +37,8 @@ def test_every_declared_symbol_is_exported(L):
             "fattn_bwd_dq", "fattn_fwd_splitkv",
             "fattn_fwd_splitkv_workspace_size", "fattn_splitkv_num_splits", "fattn_fwd_partial",
             "fattn_combine", "fattn_fwd_kouter", "fattn_fwd_kouter_workspace_size",
-            "fattn_fwd_dropout", "fattn_bwd_dropout", "fattn_fwd_blocksparse"} <= set(names)
+            "fattn_fwd_dropout", "fattn_bwd_dropout", "fattn_fwd_blocksparse",
+            "fattn_bwd_blocksparse"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
         assert getattr(fa, n) is not None
@@ -273,3 +274,17 @@ def test_blocksparse_rejects_bad_arguments(L, kw, status):
     a.update(kw)
     assert fa.fattn_fwd_blocksparse(a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 2, a["N"], a["d"], a["scale"],
                                     a["causal"], a["dtype"], a["m"]) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=None), -1), (dict(dq=None), -1), (dict(dtype=0), -4), (dict(d=96), -3), (dict(N=0), -2),
+    (dict(causal=5), -12), (dict(scale=float("nan")), -7), (dict(dq=MIS), -6), (dict(dq=P[3]), -11),
+    (dict(dk=P[10]), -11), (dict(ws=P[10]), -11), (dict(ws=None), -8), (dict(wsb=16), -8),
+])
+def test_bwd_blocksparse_rejects_bad_arguments(L, kw, status):
+    # P[10] plays the block mask: an output or the workspace equal to it is an alias
+    a = dict(m=P[10], dq=P[6], dk=P[7], ws=P[9], wsb=1 << 20, N=300, d=64, causal=0, dtype=2, scale=0.1)
+    a.update(kw)
+    m = a["m"]
+    assert fa.fattn_bwd_blocksparse(P[0], P[1], P[2], P[3], P[4], P[5], a["dq"], a["dk"], P[8], 1, 2, a["N"],
+                                    a["d"], a["scale"], a["causal"], a["dtype"], m, a["ws"], a["wsb"]) == status

@@ -1,5 +1,6 @@
-"""Block-sparse forward against the float64 block-sparse oracle (same fp16/bf16 tolerances as the
-dense forward), plus its reduction to the dense kernel on the same tile shape for an all-ones mask (bit for bit)."""
+"""Block-sparse forward and backward against the float64 block-sparse oracle (the dense path's
+fp16/bf16 tolerances: O max-abs 1e-2 and max-rel 2e-2, LSE 1e-3, gradients max-rel 5e-2), plus
+their reductions to the dense kernels for an all-ones mask (bit for bit)."""
 import math
 
 import numpy as np
@@ -101,3 +102,96 @@ def test_blocksparse_workload5_shape_sampled_heads():
     for b, h in heads:
         _check(o[b, h], lse[b, h], o_ref[b, h], lse_ref[b, h], "bf16")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+# ---------------------------------------------------------------------------------------------
+# Backward
+
+
+def _check_grads(got, ref, dtype, empty_rows=None):
+    tol = M.TOL[dtype]["grad_rel"]
+    floor = 1e-3 * max(float(np.max(np.abs(r))) for r in ref)
+    for name, x, r in zip(("dQ", "dK", "dV"), got, ref):
+        er = M.max_rel(x, r, floor=floor)
+        log(f"    {name} max-rel {er:.3e} max-abs {M.max_abs(x, r):.3e}")
+        assert np.all(np.isfinite(x)), name
+        assert er <= tol, (name, er)
+    if empty_rows is not None:
+        assert np.all(got[0][empty_rows] == 0), "dQ of rows without an allowed key"
+
+
+def _run_bwd(inp, mask, causal):
+    import torch
+    fa = _fa()
+    q, k, v, do = upload(inp)
+    m = torch.from_numpy(np.ascontiguousarray(mask)).cuda()
+    o, lse = fa.forward_blocksparse(q, k, v, m, causal=causal)
+    dq, dk, dv = fa.backward_blocksparse(q, k, v, o, do, lse, m, causal=causal)
+    torch.cuda.synchronize()
+    return from_dev(dq), from_dev(dk), from_dev(dv), from_dev(lse)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [100, 300, 700])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("density,diag", [(0.3, True), (0.6, False)])
+def test_blocksparse_backward_small_shapes(dtype, d, N, causal, density, diag):
+    B, H = 1, 3
+    nb = (N + 127) // 128
+    log(f"blocksparse bwd dtype={dtype} d={d} N={N} causal={causal} density={density} diag={diag}")
+    inp = fi.make_inputs((B, H, N, d), dtype, 1300 + N, with_do=True)
+    mask = fi.block_mask(B, H, nb, density, 1300 + N + d, diagonal=diag)
+    dq, dk, dv, lse = _run_bwd(inp, mask, causal)
+    ref = obs.backward(inp.q, inp.k, inp.v, inp.do, 1 / math.sqrt(d), mask, causal)
+    _check_grads((dq, dk, dv), ref, dtype, empty_rows=~np.isfinite(lse))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_blocksparse_backward_all_ones_is_the_dense_backward(d, causal):
+    import torch
+    fa = _fa()
+    N = 777
+    inp = fi.make_inputs((2, 2, N, d), "bf16", 1400 + d, with_do=True)
+    q, k, v, do = upload(inp)
+    nb = (N + 127) // 128
+    m = torch.ones((2, 2, nb, nb), dtype=torch.uint8, device="cuda")
+    o, lse = fa.forward(q, k, v, causal=causal)
+    g1 = fa.backward_blocksparse(q, k, v, o, do, lse, m, causal=causal)
+    g2 = fa.backward(q, k, v, o, do, lse, causal=causal)
+    torch.cuda.synchronize()
+    for x, y in zip(g1, g2):
+        assert torch.equal(x, y)
+
+
+def test_blocksparse_backward_empty_mask_and_single_block():
+    import torch
+    fa = _fa()
+    N, d = 300, 128
+    inp = fi.make_inputs((1, 1, N, d), "bf16", 1500, with_do=True)
+    q, k, v, do = upload(inp)
+    m = torch.zeros((1, 1, 3, 3), dtype=torch.uint8, device="cuda")
+    o, lse = fa.forward_blocksparse(q, k, v, m)
+    g = fa.backward_blocksparse(q, k, v, o, do, lse, m)
+    torch.cuda.synchronize()
+    assert all(torch.all(x == 0) for x in g)
+    m[0, 0, 2, 1] = 1  # only queries 256.. see keys 128..255
+    mask = m.cpu().numpy()
+    dq, dk, dv, lse = _run_bwd(inp, mask, False)
+    ref = obs.backward(inp.q, inp.k, inp.v, inp.do, 1 / math.sqrt(d), mask, False)
+    _check_grads((dq, dk, dv), ref, "bf16", empty_rows=~np.isfinite(lse))
+    assert np.all(dk[0, 0, :128] == 0) and np.all(dk[0, 0, 256:] == 0)
+
+
+def test_blocksparse_backward_workload5_shape_sampled_heads():
+    w = fi.WORKLOADS[5]
+    inp = fi.workload_inputs(5)
+    nb = w.N // 128
+    mask = fi.block_mask(w.B, w.H, nb, 0.25, 5)
+    log("blocksparse bwd B=2 H=16 N=4096 d=128 causal, density 0.25 + diagonal")
+    dq, dk, dv, _ = _run_bwd(inp, mask, True)
+    heads = sample_heads(w.B, w.H)
+    ref = obs.backward(inp.q, inp.k, inp.v, inp.do, w.scale, mask, True, heads=heads)
+    for b, h in heads:
+        _check_grads((dq[b, h], dk[b, h], dv[b, h]), tuple(r[b, h] for r in ref), "bf16")
