@@ -162,9 +162,11 @@ int fattn_bwd_blocksparse(const void* q, const void* k, const void* v, const voi
                           void* stream);
 
 /*
- * The three stages of fattn_bwd, in the order fattn_bwd enqueues them, for callers that want to
- * schedule or time them separately. Same conventions and checks as fattn_bwd; `dvec` is the
- * float32 [B,H,N] row vector D = rowsum(dO * O) (the first bytes of fattn_bwd's workspace).
+ * The backward split into three stages, for callers that want to schedule or time them
+ * separately; run in this order they give fattn_bwd's results bit for bit (fattn_bwd itself runs
+ * the dQ stage first, computing D on the way, then dK/dV). Same conventions and checks as
+ * fattn_bwd; `dvec` is the float32 [B,H,N] row vector D = rowsum(dO * O) (the first bytes of
+ * fattn_bwd's workspace).
  *   fattn_bwd_preprocess: reads o, dO; writes dvec.
  *   fattn_bwd_dkdv:       reads q, k, v, dO, lse, dvec; writes dk, dv (per key tile, recomputing
  *                         P = exp(S - LSE) once for every query tile on or below the diagonal;

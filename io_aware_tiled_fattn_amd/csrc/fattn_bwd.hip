@@ -9,7 +9,7 @@
 //     dV = P^T dO,  dP = dO V^T,  D_i = sum_t dO[i,t] O[i,t],  dS = P * (dP - D),
 //     dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Three kernels, all in stream order:
+// Three kernels (fattn_bwd runs 3 then 2: the dQ kernel also computes D and writes it for 2):
 //  1. bwd_pre:   D = rowsum(dO * O) (float32 workspace), one pass over O and dO.
 //  2. bwd_dkdv_pair: one work-group per (b*h, 128-key tile); waves p and p + 4 share 32 keys:
 //               the first keeps K in registers and accumulates dV (S, P, dV += P^T dO), the
@@ -23,6 +23,8 @@
 //               dP^T = V dO^T give each lane ONE query (its LSE and D are per-lane scalars);
 //               dQ^T += K^T dS^T takes K^T from the row-major K tile via the transposed read.
 // Every kernel writes its outputs once; there are no atomics, so results are deterministic.
+#include <type_traits>
+
 #include "fattn_device.hpp"
 #include "fattn_launch.hpp"
 
@@ -41,7 +43,7 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  const float* dvec;
+  float* dvec;  // D = rowsum(dO * O): read, or written by the dQ kernel that computes it
   int N;
   int ntiles;   // tiles per head along the grid's sequence axis
   int bh_total; // B * H
@@ -62,6 +64,19 @@ __device__ inline float to_f32<F16>(uint16_t x) { return (float)__builtin_bit_ca
 // ---------------------------------------------------------------------------------------------
 // 1. D = rowsum(dO * O): D/8 threads per row, 16-byte loads.
 
+// Sum of the 8 products of one 16-byte chunk of O and dO, in a fixed order (the dQ kernel's own
+// computation of D must match this kernel bit for bit).
+template <typename TR>
+__device__ inline float chunk_dot(u32x4 a, u32x4 b) {
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sum = fmaf(to_f32<TR>((uint16_t)(a[i] & 0xffff)), to_f32<TR>((uint16_t)(b[i] & 0xffff)), sum);
+    sum = fmaf(to_f32<TR>((uint16_t)(a[i] >> 16)), to_f32<TR>((uint16_t)(b[i] >> 16)), sum);
+  }
+  return sum;
+}
+
 template <typename TR, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                       const uint16_t* __restrict__ dO,
@@ -73,12 +88,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   if (row < rows) {
     const u32x4 a = *(const u32x4*)(o + row * D + part * 8);
     const u32x4 b = *(const u32x4*)(dO + row * D + part * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sum += to_f32<TR>((uint16_t)(a[i] & 0xffff)) * to_f32<TR>((uint16_t)(b[i] & 0xffff));
-      sum += to_f32<TR>((uint16_t)(a[i] >> 16)) * to_f32<TR>((uint16_t)(b[i] >> 16));
-    }
+    sum = chunk_dot<TR>(a, b);
   }
+  // the tree the dQ kernel reproduces when it computes D itself: partner chunks p ^ TPR/2, ...
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, TPR);
   if (row < rows && part == 0) dvec[row] = sum;
@@ -465,7 +477,10 @@ struct DqCfg {
 // SPARSE: block-sparse attention over 128 x 128 (query, key) blocks: the work-group loads the key
 // tiles whose mask column is set for either of its two mask rows, and each wave computes the ones
 // its own mask row allows.
-template <typename TR, int D, bool CAUSAL, bool BIG, bool DROP, bool SPARSE>
+// WITH_D: compute D = rowsum(dO * O) of the wave's rows here (from the dO fragments already in
+// registers and the O rows) instead of reading it, and write it for the dK/dV kernel; the result
+// is the preprocess kernel's bit for bit (same chunk sums, same pairing tree).
+template <typename TR, int D, bool CAUSAL, bool BIG, bool DROP, bool SPARSE, bool WITH_D>
 __global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BwdArgs a) {
   using Cfg = DqCfg<D>;
   using vec8 = typename TR::vec8;
@@ -505,7 +520,26 @@ __global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)
     df[s] = bitcast<vec8>(dr);
   }
   const float lse2 = qrow < N ? a.lse[(size_t)bh * N + qrow] * kLog2e : __builtin_inff();
-  const float dval = qrow < N ? a.dvec[(size_t)bh * N + qrow] : 0.f;
+  float dval;
+  if constexpr (WITH_D) {
+    // lane (h, lr) holds chunks p = 2s + h of its row; the preprocess tree pairs chunk p with
+    // p ^ D/16, then p ^ D/32, ..., within the lane, and finally p ^ 1 across the two halves
+    float ps[D / 16];
+#pragma unroll
+    for (int s2 = 0; s2 < D / 16; ++s2) {
+      u32x4 orw = {0u, 0u, 0u, 0u};
+      if (qrow < N) orw = *(const u32x4*)(a.o + head + (size_t)qrow * D + 16 * s2 + 8 * h);
+      ps[s2] = chunk_dot<TR>(orw, bitcast<u32x4>(df[s2]));
+    }
+#pragma unroll
+    for (int off = D / 32; off >= 1; off >>= 1)
+#pragma unroll
+      for (int s2 = 0; s2 < off; ++s2) ps[s2] = ps[s2] + ps[s2 + off];
+    dval = sum_halves(ps[0]);
+    if (qrow < N && h == 0) a.dvec[(size_t)bh * N + qrow] = dval;
+  } else {
+    dval = qrow < N ? a.dvec[(size_t)bh * N + qrow] : 0.f;
+  }
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -687,17 +721,9 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
   const long long BH = (long long)r.B * r.H;
   const long long rows = BH * r.N;
 
-  hipError_t e = hipSuccess;
-  if (stage < 0 || stage == 0) {
-    constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_pre_kernel<TR, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
-                       a.o, a.dO, r.dvec, rows);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const bool big = (size_t)r.N * D * 2 >= ((size_t)1 << 31);
   a.bh_total = (int)BH;
-  if (stage < 0 || stage == 1) {
+  auto dkdv = [&]() {
     a.ntiles = (r.N + PairCfg<D>::BKV - 1) / PairCfg<D>::BKV;
     dim3 gp((unsigned)(BH * a.ntiles));
     auto gop = [&](auto kern) { hipLaunchKernelGGL(kern, gp, dim3(PairCfg<D>::NT), 0, st, a); };
@@ -705,22 +731,32 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
       big ? gop(bwd_dkdv_pair_kernel<TR, D, true, true, DROP, SPARSE>) : gop(bwd_dkdv_pair_kernel<TR, D, true, false, DROP, SPARSE>);
     else
       big ? gop(bwd_dkdv_pair_kernel<TR, D, false, true, DROP, SPARSE>) : gop(bwd_dkdv_pair_kernel<TR, D, false, false, DROP, SPARSE>);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (stage < 0 || stage == 2) {
+    return hipGetLastError();
+  };
+  auto dq = [&](auto with_d) {
+    constexpr bool WD = decltype(with_d)::value;
     a.ntiles = (r.N + DqCfg<D>::BQ - 1) / DqCfg<D>::BQ;
     dim3 g2((unsigned)(BH * a.ntiles));
-    if (r.causal) {
-      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, true, DROP, SPARSE>), g2, dim3(DqCfg<D>::NT), 0, st, a);
-      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, true, false, DROP, SPARSE>), g2, dim3(DqCfg<D>::NT), 0, st, a);
-    } else {
-      if (big) hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, true, DROP, SPARSE>), g2, dim3(DqCfg<D>::NT), 0, st, a);
-      else hipLaunchKernelGGL((bwd_dq_kernel<TR, D, false, false, DROP, SPARSE>), g2, dim3(DqCfg<D>::NT), 0, st, a);
-    }
-    e = hipGetLastError();
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, g2, dim3(DqCfg<D>::NT), 0, st, a); };
+    if (r.causal)
+      big ? go(bwd_dq_kernel<TR, D, true, true, DROP, SPARSE, WD>) : go(bwd_dq_kernel<TR, D, true, false, DROP, SPARSE, WD>);
+    else
+      big ? go(bwd_dq_kernel<TR, D, false, true, DROP, SPARSE, WD>) : go(bwd_dq_kernel<TR, D, false, false, DROP, SPARSE, WD>);
+    return hipGetLastError();
+  };
+  if (stage < 0) {
+    // the whole backward: dQ first, computing D on the way, then dK/dV (which reads D)
+    hipError_t e = dq(std::true_type{});
+    return e != hipSuccess ? e : dkdv();
   }
-  return e;
+  if (stage == 0) {
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL((bwd_pre_kernel<TR, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
+                       a.o, a.dO, r.dvec, rows);
+    return hipGetLastError();
+  }
+  if (stage == 1) return dkdv();
+  return dq(std::false_type{});
 }
 
 }  // namespace
