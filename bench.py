@@ -329,8 +329,9 @@ def main(argv=None):
     # threads: 512 per work-group; forward and dQ 256 rows per group, dK/dV 128 keys.
     kernels = {
         "fwd": ("fwd_kernel", f_fwd, 1024 * 256, "fwd_kernel<Bf16, 128, 256, 128, 2, true, false, false, false>"),
-        "dkdv": ("bwd_dkdv_pair_kernel", 2 * f_fwd, 1024 * 512, "bwd_dkdv_pair_kernel<Bf16, 128, true, false, false>"),
-        "dq": ("bwd_dq_kernel", 1.5 * f_fwd, 1024 * 256, "bwd_dq_kernel<Bf16, 128, true, false, false>"),
+        "dkdv": ("bwd_dkdv_pair_kernel", 2 * f_fwd, 1024 * 512,
+                 "bwd_dkdv_pair_kernel<Bf16, 128, true, false, false, false>"),
+        "dq": ("bwd_dq_kernel", 1.5 * f_fwd, 1024 * 256, "bwd_dq_kernel<Bf16, 128, true, false, false, false, false>"),
     }
     dom = max(kernels, key=lambda k_: ms[k_])
     name, fl, grid, sig = kernels[dom]
