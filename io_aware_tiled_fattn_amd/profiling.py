@@ -145,9 +145,9 @@ def write_summaries(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
     titles = {
         workload: (f"bench.py step workload ({workload}), the B=4 forward and the K-outer ablation",
                    "The forward kernel's calls mix the B=2 (step), B=4 (prefill, every tile) and "
-                   "B=1 H=32 N=16384 (long-context) workloads, and the dQ kernel's the step's "
-                   "backward and its stage-by-stage timing; bench.py times each live with HIP "
-                   "events. The dK/dV kernel runs the step workload only. `ko_kernel` is the K-outer ablation on "
+                   "B=1 H=32 N=16384 (long-context) workloads; bench.py times each live with HIP "
+                   "events. The dK/dV and dQ kernels run the step workload only (the dQ instance "
+                   "that also computes D is the one fattn_bwd runs). `ko_kernel` is the K-outer ablation on "
                    "the step's forward shape, one launch per 128-key block (32 per call), so its "
                    "per-launch figures are 1/32 of a call."),
         DECODE_WORKLOAD: ("bench.py split-KV decode workloads (B=8 H=32 Nk=16384 d=128 bf16, "
