@@ -136,8 +136,13 @@ int main() {
   int dev = 0, ncu = 0;
   HC(hipGetDevice(&dev));
   HC(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+  int khz = 0;
+  HC(hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, dev));
   const int B = ncu > 0 && ncu <= 1024 ? ncu : 256;  // one group per CU
-  printf("compute units: %d; %d iterations per wave\n\n", ncu, R);
+  // dense bf16 peak = CUs x max engine clock x 4 SIMDs x (32768 FLOP per MFMA / its cycles)
+  printf("compute units: %d; max engine clock %.0f MHz; %d iterations per wave\n", ncu, khz / 1e3, R);
+  printf("bf16 MFMA peak at 32 cycles per 32x32x16 MFMA: %.1f TFLOP/s\n\n",
+         (double)ncu * khz * 1e3 * 4 * (32768.0 / 32.0) / 1e12);
   printf("| mix (per wave per iteration) | waves/SIMD | cycles/iter | units/SIMD/iter | cycles/unit |\n"
          "|---|---|---|---|---|\n");
   int rc = 0;
