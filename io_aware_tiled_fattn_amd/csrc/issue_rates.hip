@@ -36,7 +36,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int R = 2048;
 constexpr int LDS_BYTES = 65536;
 
-enum : int { LDS128 = 1, LDSTR = 2, MFMA = 4, EXP = 8, FMA = 16 };
+enum : int { LDS128 = 1, LDSTR = 2, MFMA = 4, EXP = 8, FMA = 16, LDSBW = 32, LDSTRBW = 64 };
 
 // MODE: a bit set of the instruction groups each iteration issues; SPLIT: waves 0-3 issue only the
 // MFMA group and waves 4-7 only the VALU groups (so each SIMD pairs one MFMA wave with one VALU wave).
@@ -71,6 +71,22 @@ __global__ __launch_bounds__(512) void mix(float* out, long long* cyc, float see
             (lds_i16x4*)(sm + ((lane * 8 + i * 512 + r * 64) & (LDS_BYTES - 1))));
         x[i & 3] ^= __builtin_bit_cast(uint2, y).x;
       }
+    }
+    if (MODE & LDSBW) {  // 16 independent ds_read_b128, combined only after all have been issued
+      u32x4 y[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = *(const u32x4*)(sm + ((lane * 16 + i * 1024 + r * 64) & (LDS_BYTES - 1)));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x ^= y[i];
+    }
+    if (MODE & LDSTRBW) {  // 16 independent ds_read_b64_tr_b16
+      uint32_t y[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        y[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                   (lds_i16x4*)(sm + ((lane * 8 + i * 512 + r * 64) & (LDS_BYTES - 1))))).x;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i & 3] ^= y[i];
     }
     if (do_mfma) {  // 16 MFMAs in 4 independent accumulator chains
 #pragma unroll
@@ -159,5 +175,10 @@ int main() {
   rc |= run<MFMA | EXP, true>("16 mfma (waves 0-3) / 32 exp (waves 4-7)", 512, 16, out, cyc, B);
   rc |= run<MFMA | FMA, true>("16 mfma (waves 0-3) / 64 fma (waves 4-7)", 512, 16, out, cyc, B);
   rc |= run<MFMA | LDSTR, false>("16 mfma + 8 tr reads, same wave", 512, 32, out, cyc, B);
+  // LDS bandwidth: bytes per CU per cycle = units/SIMD/iter x 4 SIMDs x 64 lanes x bytes per lane / cycles
+  rc |= run<LDSBW, false>("16 x ds_read_b128, independent", 256, 16, out, cyc, B);
+  rc |= run<LDSBW, false>("16 x ds_read_b128, independent", 512, 32, out, cyc, B);
+  rc |= run<LDSTRBW, false>("16 x ds_read_b64_tr_b16, independent", 512, 32, out, cyc, B);
+  rc |= run<MFMA | LDSBW, false>("16 mfma + 16 b128 reads, same wave", 512, 32, out, cyc, B);
   return rc;
 }
