@@ -144,8 +144,8 @@ __device__ inline int row_read_addr(int R, int c) {
 // the same 32 keys. Wave p ("A") keeps K in registers and accumulates dV: S = Q K^T,
 // P = exp(S - LSE), dV += P^T dO. Wave p + 4 ("B") keeps V and accumulates dK: dP = dO V^T,
 // dS = P (dP - D), dK += dS^T Q, taking P from A through LDS (16-bit, as rounded for the dV
-// product). B works one query tile behind A, so the two never wait for each other inside a
-// tile: while A runs tile i, B runs tile i - 1; the tiles i - 1, i and the one being fetched
+// product; with dropout, a set sign bit marks a dropped element, so only A draws the keep mask).
+// B works one query tile behind A, so the two never wait for each other inside a tile: while A runs tile i, B runs tile i - 1; the tiles i - 1, i and the one being fetched
 // (i + 1) sit in three LDS stages, and P goes through two exchange buffers. S is computed once
 // per (query, key) pair, and each wave holds one accumulator and one operand set, so two waves
 // share every SIMD and one wave's VALU work overlaps the other's MFMAs.
@@ -363,23 +363,29 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             u32x4 pu;
+            if (!DROP) {
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) pu[e2] = TR::pack2(p[8 * half + 2 * e2], p[8 * half + 2 * e2 + 1]);
-            xq[half * 64] = pu;  // P for B
-            if (DROP) {
+              for (int e2 = 0; e2 < 4; ++e2) pu[e2] = TR::pack2(p[8 * half + 2 * e2], p[8 * half + 2 * e2 + 1]);
+              xq[half * 64] = pu;  // P for B
+            } else {
+              // B gets P with the sign bit marking a dropped element (P >= 0, so the sign is
+              // free): it then needs no generator of its own; dV takes P M / (1 - p)
               const uint32_t kb = quad_keep_bits((uint32_t)key >> 2, (uint32_t)(q_base + qb * 32 + 8 * (2 * half) + 4 * h),
                                                  (uint32_t)bh, a.drop, lane);
               const uint32_t kb2 = quad_keep_bits((uint32_t)key >> 2,
                                                   (uint32_t)(q_base + qb * 32 + 8 * (2 * half + 1) + 4 * h),
                                                   (uint32_t)bh, a.drop, lane);
               const uint32_t bits = kb | (kb2 << 4);
+              u32x4 ps;
 #pragma unroll
               for (int e2 = 0; e2 < 4; ++e2) {
                 const int e = 2 * e2;
-                const float x0 = ((bits >> e) & 1u) ? p[8 * half + e] * a.drop.inv_keep : 0.f;
-                const float x1 = ((bits >> (e + 1)) & 1u) ? p[8 * half + e + 1] * a.drop.inv_keep : 0.f;
-                pu[e2] = TR::pack2(x0, x1);
+                const bool k0 = (bits >> e) & 1u, k1 = (bits >> (e + 1)) & 1u;
+                const float p0 = p[8 * half + e], p1 = p[8 * half + e + 1];
+                ps[e2] = TR::pack2(k0 ? p0 : -p0, k1 ? p1 : -p1);
+                pu[e2] = TR::pack2(k0 ? p0 * a.drop.inv_keep : 0.f, k1 ? p1 * a.drop.inv_keep : 0.f);
               }
+              xq[half * 64] = ps;
             }
             pk[half] = bitcast<vec8>(pu);
           }
@@ -387,13 +393,6 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             const u32x4 pu = xq[half * 64];
-            uint32_t bits = 0xFFu;
-            if (DROP)
-              bits = quad_keep_bits((uint32_t)key >> 2, (uint32_t)(q_base + qb * 32 + 8 * (2 * half) + 4 * h),
-                                    (uint32_t)bh, a.drop, lane) |
-                     (quad_keep_bits((uint32_t)key >> 2, (uint32_t)(q_base + qb * 32 + 8 * (2 * half + 1) + 4 * h),
-                                     (uint32_t)bh, a.drop, lane)
-                      << 4);
             u32x4 du;
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
@@ -403,13 +402,16 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
                 const int e = 8 * half + 4 * jj + 2 * r2;  // element index in s
                 float p0, p1;
                 unpack2<TR>(pu[2 * jj + r2], p0, p1);
-                float dp0 = s[e], dp1 = s[e + 1];
+                const float dp0 = s[e], dp1 = s[e + 1];
                 if (DROP) {
-                  const int bi = 4 * jj + 2 * r2;
-                  dp0 = ((bits >> bi) & 1u) ? dp0 * a.drop.inv_keep : 0.f;
-                  dp1 = ((bits >> (bi + 1)) & 1u) ? dp1 * a.drop.inv_keep : 0.f;
+                  // kept: dS = P (dP / (1 - p) - D); dropped (sign bit set, value -P):
+                  // dS = P (0 - D), which is the signed value times D
+                  const bool k0 = !(__float_as_uint(p0) >> 31), k1 = !(__float_as_uint(p1) >> 31);
+                  du[2 * jj + r2] = TR::pack2(k0 ? p0 * (dp0 * a.drop.inv_keep - d4[2 * r2]) : p0 * d4[2 * r2],
+                                              k1 ? p1 * (dp1 * a.drop.inv_keep - d4[2 * r2 + 1]) : p1 * d4[2 * r2 + 1]);
+                } else {
+                  du[2 * jj + r2] = TR::pack2(p0 * (dp0 - d4[2 * r2]), p1 * (dp1 - d4[2 * r2 + 1]));
                 }
-                du[2 * jj + r2] = TR::pack2(p0 * (dp0 - d4[2 * r2]), p1 * (dp1 - d4[2 * r2 + 1]));
               }
             }
             pk[half] = bitcast<vec8>(du);
