@@ -233,13 +233,17 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
   const int n_qt = (N + BQ - 1) / BQ;
   const int i_begin = CAUSAL ? (jt * BKV) / BQ : 0;
 
-  uint32_t off[LPT];
+  // The swizzle repeats every 16 rows: when one load instruction spans a multiple of 16 rows,
+  // load t lies exactly t*NT*16 bytes after load 0, and only load 0's offset is kept.
+  constexpr bool kPeriodic = NT % CPR == 0 && (NT / CPR) % 16 == 0;
+  uint32_t off[kPeriodic ? 1 : LPT];
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) {
+  for (int i = 0; i < (kPeriodic ? 1 : LPT); ++i) {
     const int chunk = i * NT + tid;
     const int row = chunk / CPR, pos = chunk % CPR;
     off[i] = (uint32_t)(row * D * 2 + (pos ^ swz_dual<D>(row)) * 16);
   }
+  auto off_t = [&](int t) { return kPeriodic ? off[0] + (uint32_t)(t * NT * 16) : off[t]; };
   const uint32_t head_bytes = BIG ? 0u : (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Qh, head_bytes);
   const __amdgpu_buffer_rsrc_t rdO = make_rsrc(dOh, head_bytes);
@@ -249,20 +253,29 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
   auto stage = [&](int p) { return smem + (p % NSTG) * Cfg::STAGE_B; };
   auto issue = [&](int i, int p) {
     uint8_t* st = stage(p) + w * 64 * 16;
+    const uint32_t soff = (uint32_t)(i * BQ) * (D * 2);
     if (!BIG && (i + 1) * BQ <= N) {
-      const uint32_t soff = (uint32_t)(i * BQ) * (D * 2);
 #pragma unroll
       for (int t = 0; t < LPT; ++t) {
-        buffer_lds16(rQ, st + t * NT * 16, off[t], soff);
-        buffer_lds16(rdO, st + TILE_B + t * NT * 16, off[t], soff);
+        const uint32_t add = kPeriodic ? (uint32_t)(t * NT * 16) : 0u;
+        buffer_lds16(rQ, st + t * NT * 16, kPeriodic ? off[0] : off[t], soff + add);
+        buffer_lds16(rdO, st + TILE_B + t * NT * 16, kPeriodic ? off[0] : off[t], soff + add);
+      }
+    } else if (!BIG) {
+      // ragged last tile: the whole offset goes in the lane's offset register, which the
+      // buffer's range check covers, so rows past the end read as zeros; A masks them (P = 0),
+      // so B's dS is 0 there as well
+#pragma unroll
+      for (int t = 0; t < LPT; ++t) {
+        buffer_lds16(rQ, st + t * NT * 16, off_t(t) + soff, 0u);
+        buffer_lds16(rdO, st + TILE_B + t * NT * 16, off_t(t) + soff, 0u);
       }
     } else {
-      // ragged last tile (or a huge head): rows past the end repeat row N - 1; A masks them
-      // (P = 0), so B's dS is 0 there as well
+      // a head of 2 GiB or more: 64-bit addresses, rows past the end repeat row N - 1
 #pragma unroll
       for (int t = 0; t < LPT; ++t) {
         const size_t src_row = (size_t)min(i * BQ + (t * NT + tid) / CPR, N - 1) * (D * 2);
-        const uint32_t in_row = off[t] - (uint32_t)((t * NT + tid) / CPR * D * 2);
+        const uint32_t in_row = off_t(t) - (uint32_t)((t * NT + tid) / CPR * D * 2);
         global_lds16((const uint8_t*)Qh + src_row + in_row, st + t * NT * 16);
         global_lds16((const uint8_t*)dOh + src_row + in_row, st + TILE_B + t * NT * 16);
       }
@@ -553,35 +566,50 @@ __global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)
   const int n_kv = (kv_end + BK - 1) / BK;
 
   // K tiles are read both row-wise and transposed (swz_dual); V tiles only row-wise.
-  uint32_t offK[LPT], offV[LPT];
+  // Both swizzles repeat every 16 rows: when one load instruction spans a multiple of 16 rows,
+  // load i lies exactly i*NT*16 bytes after load 0, and only load 0's offsets are kept.
+  constexpr bool kPeriodic = NT % CPR == 0 && (NT / CPR) % 16 == 0;
+  constexpr int NOFF = kPeriodic ? 1 : LPT;
+  uint32_t offK[NOFF], offV[NOFF];
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) {
+  for (int i = 0; i < NOFF; ++i) {
     const int chunk = i * NT + tid;
     const int row = chunk / CPR, pos = chunk % CPR;
     offK[i] = (uint32_t)(row * D * 2 + (pos ^ swz_dual<D>(row)) * 16);
     offV[i] = (uint32_t)(row * D * 2 + (pos ^ swz_rowread<D>(row)) * 16);
   }
+  auto off_k = [&](int i) { return kPeriodic ? offK[0] + (uint32_t)(i * NT * 16) : offK[i]; };
+  auto off_v = [&](int i) { return kPeriodic ? offV[0] + (uint32_t)(i * NT * 16) : offV[i]; };
   const uint32_t head_bytes = BIG ? 0u : (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rK = make_rsrc(Kh, head_bytes);
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(Vh, head_bytes);
   // key tile j into stage t & 1 (t = j except for block-sparse runs, which skip tiles)
   auto issue = [&](int j, int t) {
     uint8_t* st = smem + (t & 1) * Cfg::STAGE_B + w * 64 * 16;
+    const uint32_t soff = (uint32_t)(j * BK) * (D * 2);
     if (!BIG && (j + 1) * BK <= N) {
-      const uint32_t soff = (uint32_t)(j * BK) * (D * 2);
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
-        buffer_lds16(rK, st + i * NT * 16, offK[i], soff);
-        buffer_lds16(rV, st + TILE_B + i * NT * 16, offV[i], soff);
+        const uint32_t add = kPeriodic ? (uint32_t)(i * NT * 16) : 0u;
+        buffer_lds16(rK, st + i * NT * 16, kPeriodic ? offK[0] : offK[i], soff + add);
+        buffer_lds16(rV, st + TILE_B + i * NT * 16, kPeriodic ? offV[0] : offV[i], soff + add);
+      }
+    } else if (!BIG) {
+      // ragged last tile: the whole offset goes in the lane's offset register, which the
+      // buffer's range check covers, so rows past the end read as zeros (masked below)
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        buffer_lds16(rK, st + i * NT * 16, off_k(i) + soff, 0u);
+        buffer_lds16(rV, st + TILE_B + i * NT * 16, off_v(i) + soff, 0u);
       }
     } else {
-      // ragged last tile (or a huge head): rows past the end repeat row N - 1 (masked below)
+      // a head of 2 GiB or more: 64-bit addresses, rows past the end repeat row N - 1
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
         const size_t src_row = (size_t)min(j * BK + (i * NT + tid) / CPR, N - 1) * (D * 2);
         const uint32_t in_row = (uint32_t)((i * NT + tid) / CPR * D * 2);
-        global_lds16((const uint8_t*)Kh + src_row + (offK[i] - in_row), st + i * NT * 16);
-        global_lds16((const uint8_t*)Vh + src_row + (offV[i] - in_row), st + TILE_B + i * NT * 16);
+        global_lds16((const uint8_t*)Kh + src_row + (off_k(i) - in_row), st + i * NT * 16);
+        global_lds16((const uint8_t*)Vh + src_row + (off_v(i) - in_row), st + TILE_B + i * NT * 16);
       }
     }
   };

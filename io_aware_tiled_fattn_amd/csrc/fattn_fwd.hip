@@ -146,37 +146,52 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   const int n_kv = (kv_end + BC - 1) / BC;
 
   // Load i of this thread fills LDS chunk i*NT + tid of a tile: row r = chunk / CPR holds, at
-  // chunk position p = chunk % CPR, the source chunk p ^ swizzle(r).
-  uint32_t offK[LPT], offV[LPT];  // byte offsets within a tile: row * 2D + source chunk * 16
+  // chunk position p = chunk % CPR, the source chunk p ^ swizzle(r). Both swizzles repeat every
+  // 16 rows, so when one load instruction spans a multiple of 16 rows, load i lies exactly
+  // i*NT*16 bytes after load 0 in memory and in LDS, and only load 0's offsets are kept.
+  constexpr bool kPeriodic = NT % CPR == 0 && (NT / CPR) % 16 == 0;
+  constexpr int NOFF = kPeriodic ? 1 : LPT;
+  uint32_t offK[NOFF], offV[NOFF];  // byte offsets within a tile: row * 2D + source chunk * 16
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) {
+  for (int i = 0; i < NOFF; ++i) {
     const int chunk = i * NT + tid;
     const int row = chunk / CPR, pos = chunk % CPR;
     offK[i] = (uint32_t)(row * D * 2 + (pos ^ swz_rowread<D>(row)) * 16);
     offV[i] = (uint32_t)(row * D * 2 + (pos ^ swz_trread<D>(row)) * 16);
   }
+  auto off_k = [&](int i) { return kPeriodic ? offK[0] + (uint32_t)(i * NT * 16) : offK[i]; };
+  auto off_v = [&](int i) { return kPeriodic ? offV[0] + (uint32_t)(i * NT * 16) : offV[i]; };
   const uint32_t head_bytes = BIG ? 0u : (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rK = make_rsrc(Kh, head_bytes);
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(Vh, head_bytes);
   // tile j into stage stg % NS (stg = j except for block-sparse runs, which skip tiles)
   auto issue = [&](int j, int stg) {
     uint8_t* st = smem + (stg % NS) * Cfg::STAGE_B + w * 64 * 16;
+    const uint32_t soff = (uint32_t)(j * BC) * (D * 2);
     if (!BIG && (j + 1) * BC <= N) {
-      const uint32_t soff = (uint32_t)(j * BC) * (D * 2);
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
-        buffer_lds16(rK, st + i * NT * 16, offK[i], soff);
-        buffer_lds16(rV, st + TILE_B + i * NT * 16, offV[i], soff);
+        const uint32_t add = kPeriodic ? (uint32_t)(i * NT * 16) : 0u;
+        buffer_lds16(rK, st + i * NT * 16, kPeriodic ? offK[0] : offK[i], soff + add);
+        buffer_lds16(rV, st + TILE_B + i * NT * 16, kPeriodic ? offV[0] : offV[i], soff + add);
+      }
+    } else if (!BIG) {
+      // ragged last tile: the whole offset goes in the lane's offset register, which the
+      // buffer's range check covers, so rows past the end of the head read as zeros (finite;
+      // those keys are masked below)
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        buffer_lds16(rK, st + i * NT * 16, off_k(i) + soff, 0u);
+        buffer_lds16(rV, st + TILE_B + i * NT * 16, off_v(i) + soff, 0u);
       }
     } else {
-      // ragged last tile (or a huge head): rows past the end repeat row N - 1, so every LDS row
-      // holds real, finite data; those keys are masked below
+      // a head of 2 GiB or more: 64-bit addresses, rows past the end repeat row N - 1
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
         const size_t src_row = (size_t)min(j * BC + (i * NT + tid) / CPR, N - 1) * (D * 2);
         const uint32_t in_row = (uint32_t)((i * NT + tid) / CPR * D * 2);
-        global_lds16((const uint8_t*)Kh + src_row + (offK[i] - in_row), st + i * NT * 16);
-        global_lds16((const uint8_t*)Vh + src_row + (offV[i] - in_row), st + TILE_B + i * NT * 16);
+        global_lds16((const uint8_t*)Kh + src_row + (off_k(i) - in_row), st + i * NT * 16);
+        global_lds16((const uint8_t*)Vh + src_row + (off_v(i) - in_row), st + TILE_B + i * NT * 16);
       }
     }
   };

@@ -238,6 +238,67 @@ def test_causal_prefix_is_bitwise_unchanged(dtype):
     assert not torch.equal(o1[:, :, cut + 1:], o2[:, :, cut + 1:])
 
 
+def _rising(dtype, N, d, seed, rise, some_rows=False):
+    """Inputs whose logits climb along the key axis by ``rise`` (natural log units) per key.
+
+    Q[..., 0] = 1 (or, with ``some_rows``, only on every eighth block of 8 rows, 0 elsewhere) and
+    K[..., 0] = rise * j / scale: a later key tile's row max then exceeds the first tile's by far
+    more than the forward's slack, so the reference max moves and the state is rescaled on many
+    tiles instead of almost never.
+    """
+    inp = fi.make_inputs((1, 2, N, d), dtype, seed)
+    scale = 1 / math.sqrt(d)
+    q = inp.q.copy()
+    k = inp.k.copy()
+    col = np.ones(N, np.float32)
+    if some_rows:
+        col = ((np.arange(N) // 8) % 8 == 0).astype(np.float32)
+    q[..., 0] = col
+    k[..., 0] = np.float32(rise / scale) * np.arange(N, dtype=np.float32)
+    q, qb = fi.round_bits(q, dtype)
+    k, kb = fi.round_bits(k, dtype)
+    bits = dict(inp.bits)
+    bits["q"], bits["k"] = qb, kb
+    return fi.Inputs(dtype, q, k, inp.v, None, bits), scale
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("some_rows", [False, True])
+def test_forward_rising_logits(dtype, d, causal, some_rows):
+    # the row max grows by ~0.04 per key, 40 over the sequence: far past the first key tile's
+    inp, scale = _rising(dtype, 1000, d, 21, 0.04, some_rows)
+    o, lse = _run(inp, causal)
+    o_ref, lse_ref = att.forward(inp.q, inp.k, inp.v, scale, causal)
+    # rows that weight the last few keys have |O| near 1, where rounding O to 8 significant bits
+    # costs 2^-8 |O| (as for sharp softmaxes above)
+    f_o = max(1.0, 2.0 ** -7 * float(np.max(np.abs(o_ref))) / M.TOL[dtype]["o_abs"])
+    _check(o, lse, o_ref, lse_ref, dtype, o_abs_factor=f_o)
+
+
+@pytest.mark.parametrize("tile", [(256, 128), (128, 64), (64, 128)])
+def test_causal_prefix_bitwise_with_rising_logits(tile):
+    # rows up to the cut keep every bit when the keys after it change, also when other rows of
+    # their work-group (those past the cut) keep moving their reference max
+    import torch
+    fa = _fa()
+    inp, scale = _rising("bf16", 900, 128, 22, 0.0, some_rows=False)
+    ramp, _ = _rising("bf16", 900, 128, 22, 0.04, some_rows=False)
+    q, k, v, _ = upload(inp)
+    _, kr, _, _ = upload(ramp)
+    cut = 300
+    o1, l1 = fa.forward(q, k, v, causal=True, Br=tile[0], Bc=tile[1])
+    k2 = k.clone()
+    k2[:, :, cut + 1:] = kr[:, :, cut + 1:]
+    o2, l2 = fa.forward(q, k2, v, causal=True, Br=tile[0], Bc=tile[1])
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :, : cut + 1], o2[:, :, : cut + 1])
+    assert torch.equal(l1[:, :, : cut + 1], l2[:, :, : cut + 1])
+    # the rows past the cut did see the rising keys
+    assert float((l2[:, :, cut + 1:] - l1[:, :, cut + 1:]).min()) > 1.0
+
+
 def test_k_zero_gives_prefix_means_at_full_shape():
     import torch
     fa = _fa()
