@@ -305,6 +305,16 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
         acc[b] = TR::mma(bitcast<vec8>(both), pf[c], acc[b]);
       }
     }
+    // order: every exponential first, then the V^T reads of the first two MFMA chunks, then each
+    // MFMA with the two reads of a later one (the reads lead by four MFMAs)
+    __builtin_amdgcn_sched_group_barrier(0x002, 1000, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < BC / 16 * (D / 32) - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
 
   // The tile loop leaves as soon as some row's max outgrows the slack; the rescale (rare) is
