@@ -30,6 +30,18 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 
 
+def traffic_fields(rec):
+    """Roofline fields from one profiles/traffic.json record: ``traffic`` is the kernel's HBM bytes
+    per launch (FETCH_SIZE + WRITE_SIZE, each scaled by the calibration copy's reading), with its
+    two parts and, when that counter pass was taken, the MFMA-busy fraction."""
+    out = {"traffic": round(rec["fetch_bytes"] + rec["write_bytes"]),
+           "traffic_fetch_bytes": round(rec["fetch_bytes"]), "traffic_write_bytes": round(rec["write_bytes"]),
+           "traffic_source": "profiles/traffic.json"}
+    if rec.get("mfma_busy") is not None:
+        out["mfma_busy"] = round(rec["mfma_busy"], 4)
+    return out
+
+
 def flops_fwd(B, H, N, d, causal):
     f = 4.0 * B * H * N * N * d
     return f / 2 if causal else f
@@ -285,14 +297,13 @@ def main(argv=None):
         out_b = bh * wd.Nq * (wd.d * 2 + 4)
         part_b = S * bh * wd.Nq * (wd.d + 1) * 4
         gbs = lambda nbytes, t_ms: nbytes / (t_ms * 1e-3) / 1e9
-        dtraffic = None
-        if tr_all:
-            sig_d = "splitkv_kernel<Bf16, 128, 32, 3, true, false>"
+        dtraffic = {"traffic": None}
+        if tr_all and ident == 6:
+            sig_d = "splitkv_kernel<Bf16, 128, 32, "
             grid_d = bh * ((wd.Nq + 31) // 32) * S * 64
             for (kname, kgrid), rec in tr_all.items():
-                if kname.startswith(sig_d) and kgrid == grid_d and ident == 6:
-                    dtraffic = {"fetch_bytes": round(rec["fetch_bytes"]), "write_bytes": round(rec["write_bytes"]),
-                                "source": "profiles/traffic.json"}
+                if kname.startswith(sig_d) and kgrid == grid_d:
+                    dtraffic = traffic_fields(rec)
         path_gbs = gbs(kv_b + q_b + out_b, t_all)
         part_gbs = gbs(kv_b + q_b + part_b, t_part)
         decode[f"w{ident}"] = {
@@ -304,7 +315,7 @@ def main(argv=None):
             "roofline": {"kernel": "splitkv_kernel (partials)", "bound": "hbm",
                          "achieved": round(part_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(part_gbs / PEAK_HBM_GBS, 4),
-                         "algorithmic_bytes_per_launch": kv_b + q_b + part_b, "traffic": dtraffic,
+                         "algorithmic_bytes_per_launch": kv_b + q_b + part_b, **dtraffic,
                          "ms_per_launch": round(t_part, 4)},
         }
     dec.clear()
@@ -336,15 +347,14 @@ def main(argv=None):
     dom = max(kernels, key=lambda k_: ms[k_])
     name, fl, grid, sig = kernels[dom]
     achieved = tf(fl, ms[dom])
-    traffic = None
+    traffic = {"traffic": None}
     if tr_all:
         for (kname, kgrid), rec in tr_all.items():
             if kname.startswith(sig) and kgrid == grid:
-                traffic = {"fetch_bytes": round(rec["fetch_bytes"]), "write_bytes": round(rec["write_bytes"]),
-                           "source": "profiles/traffic.json"}
+                traffic = traffic_fields(rec)
     roof = {"kernel": f"{sig} on B=2,H=16,N=4096", "bound": "mfma",
             "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), **traffic,
             "ms_per_launch": round(ms[dom], 4), "algorithmic_tflop_per_launch": round(fl / 1e12, 4)}
 
     f3 = flops_fwd(w3.B, w3.H, w3.N, w3.d, True)

@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output for the attention kernels (kernel times and HBM traffic).
 
-Usage, after the three profiled runs of bench.py described in ``COMMANDS`` have written their
+Usage, after the profiled runs of bench.py described in ``COMMANDS`` have written their
 CSV files under ``<run_dir>``::
 
     python -m io_aware_tiled_fattn_amd.profiling <run_dir> <profiles_dir>
@@ -36,6 +36,8 @@ COMMANDS = {
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {run}/write -o run -- "
              "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy "
              "--clock-warmup-s 0 --decode 6",
+    "mfma": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d {run}/mfma -o run -- "
+            "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --clock-warmup-s 0 --decode 6",
 }
 
 
@@ -130,6 +132,23 @@ def traffic(run_dir):
     return out, fc, wc
 
 
+def mfma_busy(run_dir):
+    """Per-(kernel, grid) mean fraction of SIMD cycles with the MFMA unit busy:
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); GRBM_GUI_ACTIVE is summed
+    over the 8 XCDs. None when the run has no such counter pass."""
+    try:
+        path = _find(run_dir, "mfma", "counter_collection.csv")
+    except FileNotFoundError:
+        return None
+    busy, bmeta = _counter_per_dispatch(path, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui, _ = _counter_per_dispatch(path, "GRBM_GUI_ACTIVE")
+    per = collections.defaultdict(list)
+    for k, v in busy.items():
+        if gui.get(k):
+            per[bmeta[k]].append(v / (gui[k] / 8.0 * 1024.0))
+    return {key: sum(v) / len(v) for key, v in per.items()}
+
+
 def _is_decode(kernel):
     return any(kernel.startswith(d) for d in DECODE_KERNELS)
 
@@ -141,6 +160,9 @@ def write_summaries(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
     os.makedirs(prof_dir, exist_ok=True)
     stats = kernel_stats(run_dir)
     tr, fc, wc = traffic(run_dir)
+    busy = mfma_busy(run_dir)
+    for t in tr:
+        t["mfma_busy"] = busy.get((t["kernel"], t["grid"])) if busy else None
     cmd_note = "Commands (from the repository root, on the GPU box; RUN is an output folder):\n\n"
     titles = {
         workload: (f"bench.py step workload ({workload}), the B=4 forward and the K-outer ablation",
@@ -168,17 +190,21 @@ def write_summaries(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
         with open(os.path.join(prof_dir, f"kernel_times_{wl}.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
 
+        cmds = "    " + COMMANDS["fetch"].format(run="RUN") + "\n    " + COMMANDS["write"].format(run="RUN")
+        if busy:
+            cmds += "\n    " + COMMANDS["mfma"].format(run="RUN")
         lines = [f"# HBM traffic per launch — {title}\n",
-                 cmd_note + "    " + COMMANDS["fetch"].format(run="RUN") + "\n    " +
-                 COMMANDS["write"].format(run="RUN") + "\n",
+                 cmd_note + cmds + "\n",
                  f"Calibration (elementwise copy, 256 MiB read + 256 MiB written): FETCH_SIZE reads "
                  f"{fc:.3f} x true bytes, WRITE_SIZE reads {wc:.3f} x; the figures below are divided by "
-                 f"those factors.\n",
-                 "| kernel | grid | fetched MiB | written MiB |", "|---|---|---|---|"]
+                 f"those factors." + (" MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs "
+                                      "x 1024 SIMDs), from the third run.\n" if busy else "\n"),
+                 "| kernel | grid | fetched MiB | written MiB | MFMA busy |", "|---|---|---|---|---|"]
         for t in tr:
             if pick(t["kernel"]):
+                mb = f"{t['mfma_busy']:.1%}" if t.get("mfma_busy") is not None else "—"
                 lines.append(f"| `{t['kernel']}` | {t['grid']} | {t['fetch_bytes'] / 2**20:.1f} | "
-                             f"{t['write_bytes'] / 2**20:.1f} |")
+                             f"{t['write_bytes'] / 2**20:.1f} | {mb} |")
         with open(os.path.join(prof_dir, f"hbm_traffic_{wl}.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
     with open(os.path.join(prof_dir, "traffic.json"), "w") as f:
@@ -199,23 +225,15 @@ def _fit_exponent(ns, ys):
 def write_sweep(run_dir, prof_dir, times=None, bh=16, d=128):
     """profiles/hbm_scaling_fwd_bh16d128_bf16.md from the three sweep runs (fetch, write, mfma)."""
     tr, fc, wc = traffic(run_dir)
-    busy, bmeta = _counter_per_dispatch(_find(run_dir, "mfma", "counter_collection.csv"), "SQ_VALU_MFMA_BUSY_CYCLES")
-    gui, _ = _counter_per_dispatch(_find(run_dir, "mfma", "counter_collection.csv"), "GRBM_GUI_ACTIVE")
-    mfma = collections.defaultdict(list)
-    for k, v in busy.items():
-        name, grid = bmeta[k]
-        # GRBM_GUI_ACTIVE is summed over the 8 XCDs; 1024 SIMDs in all
-        if gui.get(k):
-            mfma[(name, grid)].append(v / (gui[k] / 8.0 * 1024.0))
+    mfma = mfma_busy(run_dir) or {}
     rows = []
     for t in tr:
         if not t["kernel"].startswith("fwd_kernel"):
             continue
         n = t["grid"] // 512 * 256 // bh  # 256 query rows per 512-thread work-group
         causal = ", true, false, false, false>" in t["kernel"]
-        busy_f = mfma.get((t["kernel"], t["grid"]))
         rows.append({"N": n, "causal": causal, "fetch": t["fetch_bytes"], "write": t["write_bytes"],
-                     "mfma_busy": sum(busy_f) / len(busy_f) if busy_f else None})
+                     "mfma_busy": mfma.get((t["kernel"], t["grid"]))})
     rows.sort(key=lambda r: (r["causal"], r["N"]))
     lines = ["# HBM bytes versus N — forward, B=1 H=16 d=128 bf16 (256 x 128 tiles)\n",
              "Commands (from the repository root, on the GPU box; RUN is an output folder):\n"]
