@@ -47,6 +47,7 @@ struct BwdArgs {
   int N;
   int ntiles;   // tiles per head along the grid's sequence axis
   int bh_total; // B * H
+  int hgroup;   // causal grid order: heads of an XCD taken this many at a time
   float c;      // scale * log2(e) (signed)
   float scale;  // signed softmax scale
   DropParams drop;  // dropout on P (DROP instances only)
@@ -104,13 +105,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // run first across all heads of an XCD: for dK/dV that is the first key tile (it sees every query
 // tile), for dQ the last query tile.
 __device__ inline void bwd_block_coords(int bid, int nblocks, int ntiles, int bh_total, bool causal,
-                                        bool long_is_low, int* bh, int* t) {
+                                        bool long_is_low, int hgroup, int* bh, int* t) {
   if ((bh_total & 7) == 0) {
     const int hpx = bh_total >> 3;
     const int xcd = bid & 7, local = bid >> 3;
     if (causal) {
-      const int r = local / hpx;
-      *bh = xcd * hpx + (local - r * hpx);
+      int hh, r;
+      causal_xcd_order(local, hpx, ntiles, hgroup, &hh, &r);
+      *bh = xcd * hpx + hh;
       *t = long_is_low ? r : ntiles - 1 - r;
     } else {
       const int hh = local / ntiles;
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
   const int N = a.N;
 
   int bh, jt;
-  bwd_block_coords(blockIdx.x, gridDim.x, a.ntiles, a.bh_total, CAUSAL, true, &bh, &jt);
+  bwd_block_coords(blockIdx.x, gridDim.x, a.ntiles, a.bh_total, CAUSAL, true, a.hgroup, &bh, &jt);
   const size_t head = (size_t)bh * (size_t)N * D;
   const size_t rowbase = (size_t)bh * (size_t)N;
   const uint16_t* __restrict__ Qh = a.q + head;
@@ -511,7 +513,7 @@ __global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)
   const int N = a.N;
 
   int bh, qt;
-  bwd_block_coords(blockIdx.x, gridDim.x, a.ntiles, a.bh_total, CAUSAL, false, &bh, &qt);
+  bwd_block_coords(blockIdx.x, gridDim.x, a.ntiles, a.bh_total, CAUSAL, false, a.hgroup, &bh, &qt);
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* __restrict__ Kh = a.k + head;
   const uint16_t* __restrict__ Vh = a.v + head;
@@ -753,6 +755,7 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
 
   const bool big = (size_t)r.N * D * 2 >= ((size_t)1 << 31);
   a.bh_total = (int)BH;
+  a.hgroup = head_group(a.bh_total);
   auto dkdv = [&]() {
     a.ntiles = (r.N + PairCfg<D>::BKV - 1) / PairCfg<D>::BKV;
     dim3 gp((unsigned)(BH * a.ntiles));

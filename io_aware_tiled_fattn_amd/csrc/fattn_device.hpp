@@ -184,6 +184,19 @@ __device__ inline uint32_t quad_keep_bits(uint32_t kgroup, uint32_t q4, uint32_t
          (((quad_bcast<2>(m) >> r) & 1u) << 2) | (((quad_bcast<3>(m) >> r) & 1u) << 3);
 }
 
+// Causal grid order within one XCD: its hpx heads are taken `group` at a time, and inside a group
+// the tiles of all its heads run longest first (rank 0 = longest), so the triangular work stays
+// balanced while at most `group` heads' K/V (or Q/dO) compete for the XCD's L2. `local` runs over
+// hpx * ntiles values; every (head, rank) pair comes out exactly once.
+__device__ inline void causal_xcd_order(int local, int hpx, int ntiles, int group, int* head, int* rank) {
+  const int G = group < 1 ? 1 : (group > hpx ? hpx : group);
+  const int g = local / (G * ntiles);
+  const int rem = local - g * G * ntiles;
+  const int Gg = min(G, hpx - g * G);  // the last group may hold fewer heads
+  *rank = rem / Gg;
+  *head = g * G + (rem - *rank * Gg);
+}
+
 // Block index remap so that consecutive logical blocks share an XCD: hardware dispatches block
 // ids round-robin over the 8 XCDs, so physical id x runs on XCD x % 8. When the grid is a
 // multiple of 8 the logical order visits, per XCD, one contiguous range of work.

@@ -28,9 +28,10 @@
 //    is only moved when a row's max grows by more than kRescaleSlack (2^8): the factor is then
 //    exactly 1 for almost every tile (page 2, tips), the exp2 arguments stay <= 8, and the result
 //    is unchanged because O and l always share the same reference max.
-//  * Work-group order: the 8 XCDs each take a contiguous range of heads; with the causal mask the
-//    query tiles of those heads run longest first (all heads' last tiles, then the ones before),
-//    which balances the triangular work across CUs.
+//  * Work-group order: the 8 XCDs each take a contiguous range of heads; with the causal mask an
+//    XCD takes its heads four at a time and runs their query tiles longest first (the group's
+//    last tiles, then the ones before), which balances the triangular work across CUs while only
+//    four heads' K/V compete for the XCD's L2.
 #include "fattn_device.hpp"
 #include "fattn_launch.hpp"
 
@@ -50,6 +51,7 @@ struct FwdArgs {
   int N;
   int n_qtiles;
   int bh_total;        // B * H
+  int hgroup;          // causal grid order: heads of an XCD taken this many at a time
   float c;             // |scale| * log2(e), > 0
   uint32_t neg_mask;   // 0x80008000 flips the sign of two packed 16-bit Q elements (scale < 0)
   uint32_t keep_mask;  // 0 zeroes Q (scale == 0: every logit is 0), else all ones
@@ -61,13 +63,14 @@ struct FwdArgs {
 // Block id -> (head, query tile). Hardware deals block ids round-robin over the 8 XCDs, so
 // block x runs on XCD x % 8; each XCD is given a contiguous range of heads.
 __device__ inline void fwd_block_coords(int bid, int nblocks, int n_qtiles, int bh_total, bool causal,
-                                        int* bh, int* qt) {
+                                        int hgroup, int* bh, int* qt) {
   if ((bh_total & 7) == 0) {
     const int hpx = bh_total >> 3;
     const int xcd = bid & 7, local = bid >> 3;
     if (causal) {
-      const int r = local / hpx;  // rank of the tile length, longest first
-      *bh = xcd * hpx + (local - r * hpx);
+      int hh, r;  // r: rank of the tile length, longest first
+      causal_xcd_order(local, hpx, n_qtiles, hgroup, &hh, &r);
+      *bh = xcd * hpx + hh;
       *qt = n_qtiles - 1 - r;
     } else {
       const int hh = local / n_qtiles;
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   const int N = a.N;
 
   int bh, qt;
-  fwd_block_coords(blockIdx.x, gridDim.x, a.n_qtiles, a.bh_total, CAUSAL, &bh, &qt);
+  fwd_block_coords(blockIdx.x, gridDim.x, a.n_qtiles, a.bh_total, CAUSAL, a.hgroup, &bh, &qt);
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* __restrict__ Qh = a.q + head;
   const uint16_t* __restrict__ Kh = a.k + head;
@@ -621,6 +624,7 @@ hipError_t launch16(const FwdReq& r, hipStream_t st) {
   a.N = r.N;
   a.n_qtiles = (r.N + BR - 1) / BR;
   a.bh_total = r.B * r.H;
+  a.hgroup = head_group(a.bh_total);
   a.c = r.scale == 0.f ? 1.f : fabsf(r.scale) * kLog2e;
   a.neg_mask = r.scale < 0.f ? 0x80008000u : 0u;
   a.keep_mask = r.scale == 0.f ? 0u : 0xffffffffu;

@@ -238,6 +238,17 @@ def test_causal_prefix_is_bitwise_unchanged(dtype):
     assert not torch.equal(o1[:, :, cut + 1:], o2[:, :, cut + 1:])
 
 
+@pytest.mark.parametrize("B,H", [(3, 16), (5, 8)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_order_with_a_partial_head_group(B, H, causal):
+    # causal work-groups of an XCD run four heads at a time; 6 and 5 heads per XCD leave a last
+    # group of 2 and 1: every head must still get each of its query tiles exactly once
+    inp = fi.make_inputs((B, H, 700, 128), "bf16", 31)
+    o, lse = _run(inp, causal)
+    o_ref, lse_ref = att.forward(inp.q, inp.k, inp.v, 1 / math.sqrt(128), causal)
+    _check(o, lse, o_ref, lse_ref, "bf16")
+
+
 def _rising(dtype, N, d, seed, rise, some_rows=False):
     """Inputs whose logits climb along the key axis by ``rise`` (natural log units) per key.
 
