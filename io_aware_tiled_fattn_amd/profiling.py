@@ -156,6 +156,36 @@ def _is_decode(kernel):
 DECODE_WORKLOAD = "decode_b8h32nk16384d128_bf16"
 
 
+# bench.py's per-kernel HIP-event times (kernel_ms) for the step workload, and the kernels they time
+# (its dQ figure times the stage entry point, the instance that reads D)
+LIVE_KERNELS = {
+    "dkdv": "bwd_dkdv_pair_kernel<Bf16, 128, true, false, false, false>",
+    "dq": "bwd_dq_kernel<Bf16, 128, true, false, false, false, false>",
+}
+
+
+def _live_vs_trace(run_dir, stats):
+    """Lines comparing bench.py's live kernel times with the trace, when the run directory holds
+    the JSON line of a plain bench.py run made on the same box (``bench.json``)."""
+    path = os.path.join(run_dir, "bench.json")
+    if not os.path.exists(path):
+        return []
+    with open(path) as f:
+        live = json.loads(f.read().strip().splitlines()[-1])
+    out = ["", "The same box, a plain `python bench.py` run just before the trace: its HIP-event times "
+           "per launch beside the trace's average (the trace's average for a kernel that runs only "
+           "the step workload):", "", "| kernel | bench.py live ms | trace avg ms |", "|---|---|---|"]
+    for key, sig in LIVE_KERNELS.items():
+        tr = [s_ for s_ in stats if s_["kernel"].startswith(sig)]
+        if key in live.get("kernel_ms", {}) and tr:
+            out.append(f"| `{sig}` | {live['kernel_ms'][key]:.4f} | {tr[0]['avg_us'] / 1e3:.4f} |")
+    roof = live.get("roofline", {})
+    if roof:
+        out += ["", f"bench.py roofline on that run: `{roof.get('kernel')}`, {roof.get('achieved')} "
+                f"{roof.get('unit')} of {roof.get('peak')} (frac {roof.get('frac')})."]
+    return out
+
+
 def write_summaries(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
     os.makedirs(prof_dir, exist_ok=True)
     stats = kernel_stats(run_dir)
@@ -187,6 +217,8 @@ def write_summaries(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
                 lines.append(f"| `{s['kernel']}` | {s['calls']} | {s['avg_us']:.1f} | {s['min_us']:.1f} | "
                              f"{s['max_us']:.1f} | {s['pct']:.1f} |")
         lines.append("\n" + note + " % time is over every kernel of the run.")
+        if wl != DECODE_WORKLOAD:
+            lines += _live_vs_trace(run_dir, stats)
         with open(os.path.join(prof_dir, f"kernel_times_{wl}.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
 
