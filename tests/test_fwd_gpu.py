@@ -13,6 +13,7 @@ import pytest
 import fattn_inputs as fi
 from oracle import attention as att
 from oracle import metrics as M
+from oracle import splitkv as osk
 from tests.gpu_util import from_dev, log, sample_heads, to_dev, upload
 
 pytestmark = pytest.mark.gpu
@@ -324,6 +325,51 @@ def test_k_zero_gives_prefix_means_at_full_shape():
     assert float((o.float() - ref).abs().max()) <= 1e-2
     lref = torch.log(torch.arange(1, w.N + 1, device=v.device, dtype=torch.float32))
     assert float((lse - lref).abs().max()) <= 1e-3
+
+
+def test_forward_huge_head_uses_64bit_addressing():
+    # one head whose Q, K and V are 2 GiB each (N d 2 >= 2^31), causal: the 64-bit address path
+    # with a ragged last tile. Q, K and V repeat one 64-row block, so row i (query i mod 64)
+    # sees (i + 1) // 64 whole copies of the block and the first (i + 1) % 64 of its keys: the
+    # exact result is the merge of the block's result (LSE + ln copies) with that prefix's.
+    import torch
+    fa = _fa()
+    d, R = 128, (1 << 23) // 64 + 1
+    N = 64 * R + 37
+    log(f"forward huge head N={N}")
+    blk = fi.make_inputs((1, 1, 64, d), "bf16", 677)
+    qb, kb, vb, _ = upload(blk)
+    reps = lambda x: torch.cat([x[0, 0].repeat(R, 1), x[0, 0, :37]]).reshape(1, 1, N, d)
+    q, k, v = reps(qb), reps(kb), reps(vb)
+    o, lse = fa.forward(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    rows = [0, 37, 63, 64, 1000, N // 2, N - 38, N - 2, N - 1]
+    o = from_dev(o[0, 0, rows])
+    lse = from_dev(lse[0, 0, rows])
+    del q, k, v
+    scale = 1 / math.sqrt(d)
+    q64, k64, v64 = (x[0, 0].astype(np.float64) for x in (blk.q, blk.k, blk.v))
+    o_ref, lse_ref = [], []
+    for i in rows:
+        qi = q64[i % 64][None]
+        full, part = (i + 1) // 64, (i + 1) % 64
+        parts_o, parts_l = [], []
+        if full:
+            ob, lb = att.forward_slice(qi, k64, v64, scale)
+            parts_o.append(ob)
+            parts_l.append(lb + math.log(full))
+        if part:
+            op, lp = att.forward_slice(qi, k64[:part], v64[:part], scale)
+            parts_o.append(op)
+            parts_l.append(lp)
+        oi, li = osk.combine(np.stack(parts_o), np.stack(parts_l))
+        o_ref.append(oi[0])
+        lse_ref.append(li[0])
+    # Every 128-key tile of this input has the same exp-sum, and the float32 running sum adds one
+    # per tile: n equal terms summed in order drift by at most n 2^-25 relative, i.e. 2e-3 here
+    # (65,536 tiles), which the LSE bound takes on top of its 1e-3.
+    lse_tol = M.TOL["bf16"]["lse_abs"] + (N / 128) * 2.0 ** -25
+    _check(o, lse, np.array(o_ref), np.array(lse_ref), "bf16", lse_tol=lse_tol)
 
 
 def test_run_to_run_deterministic():
