@@ -117,23 +117,32 @@ FWD_TILES = ((64, 64), (64, 128), (128, 64), (128, 128), (256, 64), (256, 128))
 
 
 def n_sweep(torch, fa):
-    """Forward at N = 1024 .. 16384 (B=1, H=16, d=128, bf16), causal and non-causal: three launches
-    each (for counter runs) and a timed block each; then a 256 MiB + 256 MiB calibration copy."""
+    """Forward and backward at N = 1024 .. 16384 (B=1, H=16, d=128, bf16), causal and non-causal:
+    three launches each (for counter runs) and a timed block each; then a 256 MiB + 256 MiB
+    calibration copy."""
     gen = torch.Generator(device="cuda")
     gen.manual_seed(2024)
-    out = {"workload": "forward, B=1 H=16 d=128 bf16, N sweep", "runs": []}
+    out = {"workload": "forward and backward, B=1 H=16 d=128 bf16, N sweep", "runs": []}
     for N in SWEEP_N:
-        q, k, v = (torch.randn(1, 16, N, 128, device="cuda", dtype=torch.bfloat16, generator=gen)
-                   for _ in range(3))
+        q, k, v, do = (torch.randn(1, 16, N, 128, device="cuda", dtype=torch.bfloat16, generator=gen)
+                       for _ in range(4))
         o, lse = torch.empty_like(q), torch.empty(1, 16, N, device="cuda")
         for causal in (False, True):
             for _ in range(3):
                 fa.forward(q, k, v, causal=causal, out=o, lse=lse)
             torch.cuda.synchronize()
             ms = _time_calls(lambda: fa.forward(q, k, v, causal=causal, out=o, lse=lse), 10, 2, torch)
-            out["runs"].append({"N": N, "causal": causal, "ms": round(ms, 4),
+            out["runs"].append({"kind": "fwd", "N": N, "causal": causal, "ms": round(ms, 4),
                                 "tflops": round(flops_fwd(1, 16, N, 128, causal) / (ms * 1e-3) / 1e12, 1)})
-        del q, k, v, o, lse
+            ws = torch.empty(fa.fattn_bwd_workspace_size(1, 16, N, 128, 2), dtype=torch.uint8, device="cuda")
+            for _ in range(3):
+                fa.backward(q, k, v, o, do, lse, causal=causal, workspace=ws)
+            torch.cuda.synchronize()
+            ms = _time_calls(lambda: fa.backward(q, k, v, o, do, lse, causal=causal, workspace=ws), 5, 1, torch)
+            out["runs"].append({"kind": "bwd", "N": N, "causal": causal, "ms": round(ms, 4),
+                                "tflops": round(2.5 * flops_fwd(1, 16, N, 128, causal) / (ms * 1e-3) / 1e12, 1)})
+            del ws
+        del q, k, v, do, o, lse
     src = torch.ones(128 * 2**20, dtype=torch.bfloat16, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -157,7 +166,7 @@ def main(argv=None):
                     help="also run a plain 256 MiB read + 256 MiB write elementwise copy, so HBM "
                          "byte counters can be scaled by a kernel of known traffic")
     ap.add_argument("--n-sweep", action="store_true",
-                    help="only run the forward at N = 1024 .. 16384 (B=1, H=16, d=128, bf16, causal and "
+                    help="only run the forward and the backward at N = 1024 .. 16384 (B=1, H=16, d=128, bf16, causal and "
                          "non-causal) a few times each, plus the calibration copy, for the HBM-bytes-vs-N "
                          "counters; prints one JSON line with the per-N times")
     a = ap.parse_args(argv)

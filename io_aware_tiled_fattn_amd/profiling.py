@@ -41,7 +41,7 @@ COMMANDS = {
 }
 
 
-# HBM bytes versus N for the forward (spec evidence that traffic stays O(N d)).
+# HBM bytes versus N for the forward and the backward (evidence that traffic stays O(N d)).
 SWEEP_COMMANDS = {
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {run}/fetch -o run -- "
              "python -u bench.py --n-sweep",
@@ -255,10 +255,18 @@ def _fit_exponent(ns, ys):
 
 
 def write_sweep(run_dir, prof_dir, times=None, bh=16, d=128):
-    """profiles/hbm_scaling_fwd_bh16d128_bf16.md from the three sweep runs (fetch, write, mfma)."""
+    """profiles/hbm_scaling_fwd_bwd_bh16d128_bf16.md from the three sweep runs (fetch, write, mfma)."""
     tr, fc, wc = traffic(run_dir)
     mfma = mfma_busy(run_dir) or {}
     rows = []
+    bwd = collections.defaultdict(dict)  # (N, causal) -> {"dkdv": record, "dq": record}
+    for t in tr:
+        name = t["kernel"]
+        targs = name[name.index("<") + 1:name.index(">")].split(", ") if "<" in name else []
+        if name.startswith("bwd_dkdv_pair_kernel") and targs[3:6] == ["false"] * 3:
+            bwd[(t["grid"] // 512 * 128 // bh, targs[2] == "true")]["dkdv"] = t
+        elif name.startswith("bwd_dq_kernel") and targs[3:7] == ["false", "false", "false", "true"]:
+            bwd[(t["grid"] // 512 * 256 // bh, targs[2] == "true")]["dq"] = t
     for t in tr:
         if not t["kernel"].startswith("fwd_kernel"):
             continue
@@ -267,12 +275,13 @@ def write_sweep(run_dir, prof_dir, times=None, bh=16, d=128):
         rows.append({"N": n, "causal": causal, "fetch": t["fetch_bytes"], "write": t["write_bytes"],
                      "mfma_busy": mfma.get((t["kernel"], t["grid"]))})
     rows.sort(key=lambda r: (r["causal"], r["N"]))
-    lines = ["# HBM bytes versus N — forward, B=1 H=16 d=128 bf16 (256 x 128 tiles)\n",
+    lines = ["# HBM bytes versus N — forward and backward, B=1 H=16 d=128 bf16\n",
              "Commands (from the repository root, on the GPU box; RUN is an output folder):\n"]
     for key in ("fetch", "write", "mfma"):
         lines.append("    " + SWEEP_COMMANDS[key].format(run="RUN"))
     lines += ["", f"Counters calibrated on a 256 MiB + 256 MiB copy (FETCH_SIZE x{fc:.3f}, WRITE_SIZE x{wc:.3f}). "
               "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs).", "",
+              "Forward (256 x 128 tiles):", "",
               "| causal | N | HBM read MiB | HBM written MiB | Q+K+V+O+LSE MiB | N x N score matrix MiB (bf16) | MFMA busy |",
               "|---|---|---|---|---|---|---|"]
     for r in rows:
@@ -288,12 +297,34 @@ def write_sweep(run_dir, prof_dir, times=None, bh=16, d=128):
             e = _fit_exponent([r["N"] for r in sel], [r["fetch"] + r["write"] for r in sel])
             lines.append(f"Fitted exponent of HBM bytes in N (causal={causal}): {e:.3f} "
                          f"(the score matrix would grow with exponent 2).")
+    brows = sorted((k, v) for k, v in bwd.items() if "dkdv" in v and "dq" in v)
+    if brows:
+        lines += ["", "Backward (`fattn_bwd`: the dQ kernel, which also computes D = rowsum(dO∘O), then "
+                  "the dK/dV kernel), same runs. The one-pass minimum reads Q, K, V, O, dO once and "
+                  "writes dQ, dK, dV once: 8 N d 2 B per head, plus the float32 LSE and D.", "",
+                  "| causal | N | dQ read MiB | dK/dV read MiB | written MiB | one-pass MiB | N x N score matrix MiB (bf16) | MFMA busy dQ / dK/dV |",
+                  "|---|---|---|---|---|---|---|---|"]
+        totals = {False: [], True: []}
+        for (n, causal), v in brows:
+            dq_, kv_ = v["dq"], v["dkdv"]
+            wr = dq_["write_bytes"] + kv_["write_bytes"]
+            one = (8 * n * d * 2 + 12 * n) * bh
+            mb = lambda r: f"{mfma[(r['kernel'], r['grid'])]:.1%}" if (r["kernel"], r["grid"]) in mfma else "—"
+            lines.append(f"| {causal} | {n} | {dq_['fetch_bytes'] / 2**20:.1f} | {kv_['fetch_bytes'] / 2**20:.1f} | "
+                         f"{wr / 2**20:.1f} | {one / 2**20:.1f} | {n * n * 2 * bh / 2**20:.0f} | {mb(dq_)} / {mb(kv_)} |")
+            totals[causal].append((n, dq_["fetch_bytes"] + kv_["fetch_bytes"] + wr))
+        lines.append("")
+        for causal in (False, True):
+            sel = sorted(totals[causal])
+            if len(sel) >= 2:
+                e = _fit_exponent([x[0] for x in sel], [x[1] for x in sel])
+                lines.append(f"Fitted exponent of the backward's HBM bytes in N (causal={causal}): {e:.3f}.")
     if times:
         lines += ["", "Times from the same command's timed blocks (HIP events):", "",
-                  "| causal | N | ms | TFLOP/s |", "|---|---|---|---|"]
+                  "| pass | causal | N | ms | TFLOP/s |", "|---|---|---|---|---|"]
         for t in times:
-            lines.append(f"| {t['causal']} | {t['N']} | {t['ms']} | {t['tflops']} |")
-    with open(os.path.join(prof_dir, "hbm_scaling_fwd_bh16d128_bf16.md"), "w") as f:
+            lines.append(f"| {t.get('kind', 'fwd')} | {t['causal']} | {t['N']} | {t['ms']} | {t['tflops']} |")
+    with open(os.path.join(prof_dir, "hbm_scaling_fwd_bwd_bh16d128_bf16.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     return rows
 
