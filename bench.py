@@ -102,14 +102,23 @@ def cpu_oracle_baseline(budget_s: float = 20.0):
         att.forward(inp.q, inp.k, inp.v, w.scale, True)
         att.backward(inp.q, inp.k, inp.v, inp.do, w.scale, True)
         heads += 1
-        if time.perf_counter() - t0 > budget_s / 2 or heads >= 4:
+        if time.perf_counter() - t0 > budget_s / 2 or heads >= w.B * w.H:
             break
-    dt = (time.perf_counter() - t0) / heads
+    total = time.perf_counter() - t0
+    dt = total / heads
     fl = flops_fwd(1, 1, w.N, w.d, True) * 3.5
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads} x one (b,h) slice of B=2,H=16,N=4096,d=128 causal: fp64 forward + "
-                      f"backward, {dt:.2f} s per slice (the oracle evaluates full rows, i.e. "
-                      f"non-causal work, but is credited the causal FLOP count)"}
+            "cpu_model": model,
+            "sample": f"{heads} of the 32 (b,h) slices of B=2,H=16,N=4096,d=128 causal (the same "
+                      f"slice's inputs each time): fp64 forward + backward, {total:.1f} s in all, "
+                      f"{dt:.2f} s per slice (the oracle evaluates full rows, i.e. non-causal work, "
+                      f"but is credited the causal FLOP count)"}
 
 
 SWEEP_N = (1024, 2048, 4096, 8192, 16384)
