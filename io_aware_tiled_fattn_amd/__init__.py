@@ -200,6 +200,11 @@ def fattn_version() -> int:
 
 
 # --- torch-tensor wrappers ---------------------------------------------------------------------
+#
+# Every tensor handed to the library is checked here before any launch: it must be a contiguous
+# device tensor on q's device, of the shape and dtype the entry point reads or writes. A host
+# tensor, a wrong dtype or a short buffer would otherwise reach a kernel as a bad address or an
+# out-of-range access.
 
 
 def dtype_code(t) -> int:
@@ -210,13 +215,52 @@ def dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def _check(t, name, like=None):
-    if not t.is_cuda:
+def _check_dev(t, name, shape=None, dtype=None, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not getattr(t, "is_cuda", False):
         raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, not {t.device}")
     if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous [B, H, N, d]")
-    if like is not None and (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device):
-        raise ValueError(f"{name} must match q in shape, dtype and device")
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+
+
+def _check(t, name, like=None):
+    """A [B, H, N, d] tensor; with ``like``, of like's shape, dtype and device."""
+    if like is None:
+        _check_dev(t, name)
+        if len(t.shape) != 4:
+            raise ValueError(f"{name} must be [B, H, N, d]")
+    else:
+        _check_dev(t, name, like.shape, like.dtype, like.device)
+
+
+def _check_rows(t, name, q, n=None):
+    """A float32 [B, H, N] per-row tensor (LSE, D) for q [B, H, N, d]."""
+    import torch
+    B, H, N, _ = q.shape
+    _check_dev(t, name, (B, H, N if n is None else n), torch.float32, q.device)
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _workspace(workspace, need, device):
+    """The caller's workspace (checked: a device tensor on ``device`` of at least ``need`` bytes)
+    or a new one."""
+    import torch
+    if workspace is None:
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    _check_dev(workspace, "workspace", device=device)
+    if _nbytes(workspace) < need:
+        raise ValueError(f"workspace holds {_nbytes(workspace)} bytes, {need} needed")
+    return workspace
 
 
 def _stream(stream):
@@ -245,6 +289,7 @@ def forward(q, k, v, causal=False, scale=None, Br=0, Bc=0, out=None, lse=None, s
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check(out, "out", q)
+    _check_rows(lse, "lse", q)
     if p_drop:
         if Br or Bc:
             raise ValueError("dropout runs with the default tile shape")
@@ -262,34 +307,47 @@ def forward(q, k, v, causal=False, scale=None, Br=0, Bc=0, out=None, lse=None, s
     return out, lse
 
 
-def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, stream=None, p_drop=0.0,
-             seed=0):
-    """dQ, dK, dV for contiguous [B, H, N, d] float16/bfloat16 device tensors (with dropout of
-    ``p_drop`` and ``seed`` when p_drop > 0: the same mask as the forward)."""
+def _check_bwd_inputs(q, k, v, o, do, lse):
+    _check(q, "q")
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, q)
+    _check_rows(lse, "lse", q)
+
+
+def _grad_outputs(q, dq, dk, dv):
     import torch
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
-        _check(t, n, q if n != "q" else None)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, n, q)
+    return dq, dk, dv
+
+
+def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, stream=None, p_drop=0.0,
+             seed=0, dq=None, dk=None, dv=None):
+    """dQ, dK, dV for contiguous [B, H, N, d] float16/bfloat16 device tensors (with dropout of
+    ``p_drop`` and ``seed`` when p_drop > 0: the same mask as the forward). ``dq``, ``dk``,
+    ``dv`` may be given to write into existing tensors."""
+    _check_bwd_inputs(q, k, v, o, do, lse)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     code = dtype_code(q)
-    need = fattn_bwd_workspace_size(B, H, N, d, code)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    workspace = _workspace(workspace, fattn_bwd_workspace_size(B, H, N, d, code), q.device)
+    dq, dk, dv = _grad_outputs(q, dq, dk, dv)
     if p_drop:
         st = fattn_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                B, H, N, d, float(scale), int(bool(causal)), code, float(p_drop), int(seed),
-                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                               _stream(stream))
+                               workspace.data_ptr(), _nbytes(workspace), _stream(stream))
         if st != 0:
             raise FattnError(st, "fattn_bwd_dropout")
         return dq, dk, dv
     st = fattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                    B, H, N, d, float(scale), int(bool(causal)), code,
-                   workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+                   workspace.data_ptr(), _nbytes(workspace), _stream(stream))
     if st != 0:
         raise FattnError(st, "fattn_bwd")
     return dq, dk, dv
@@ -299,6 +357,13 @@ def backward_stages(q, k, v, o, do, lse, dq, dk, dv, dvec, causal=False, scale=N
                     stages=(0, 1, 2)):
     """Run the chosen stages of the backward (0: D = rowsum(dO*O), 1: dK/dV, 2: dQ) into
     preallocated outputs; ``dvec`` is a float32 [B, H, N] device tensor."""
+    _check_bwd_inputs(q, k, v, o, do, lse)
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, n, q)
+    _check_rows(dvec, "dvec", q)
+    for stage in stages:
+        if stage not in (0, 1, 2):
+            raise ValueError(f"unknown backward stage {stage}")
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -311,35 +376,23 @@ def backward_stages(q, k, v, o, do, lse, dq, dk, dv, dvec, causal=False, scale=N
             st = fattn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
                                 dvec.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale),
                                 int(bool(causal)), code, s)
-        elif stage == 2:
+        else:
             st = fattn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
                               dvec.data_ptr(), dq.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
                               code, s)
-        else:
-            raise ValueError(f"unknown backward stage {stage}")
         if st != 0:
             raise FattnError(st, f"backward stage {stage}")
 
 
-def _check_dev(t, name, shape=None, dtype=None):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if shape is not None and tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
-    if dtype is not None and t.dtype != dtype:
-        raise ValueError(f"{name} must be {dtype}")
-
-
 def _decode_shapes(q, k, v):
-    if q.dim() != 4 or k.dim() != 4:
+    _check_dev(q, "q")
+    _check_dev(k, "k")
+    if len(q.shape) != 4 or len(k.shape) != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
-    _check_dev(q, "q")
-    _check_dev(k, "k", (B, H, Nk, d), q.dtype)
-    _check_dev(v, "v", (B, H, Nk, d), q.dtype)
+    _check_dev(k, "k", (B, H, Nk, d), q.dtype, q.device)
+    _check_dev(v, "v", (B, H, Nk, d), q.dtype, q.device)
     return B, H, Nq, Nk, d
 
 
@@ -352,18 +405,16 @@ def forward_splitkv(q, k, v, causal=False, scale=None, num_splits=0, out=None, l
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = fattn_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, int(num_splits))
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    _check_dev(out, "out", q.shape, q.dtype)
-    _check_dev(lse, "lse", (B, H, Nq), torch.float32)
+    _check_dev(out, "out", q.shape, q.dtype, q.device)
+    _check_dev(lse, "lse", (B, H, Nq), torch.float32, q.device)
     st = fattn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                            B, H, Nq, Nk, d, float(scale), int(bool(causal)), dtype_code(q), int(num_splits),
-                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                           _stream(stream))
+                           workspace.data_ptr(), _nbytes(workspace), _stream(stream))
     if st != 0:
         raise FattnError(st, "fattn_fwd_splitkv")
     return out, lse
@@ -381,8 +432,8 @@ def forward_partial(q, k, v, num_splits, causal=False, scale=None, o_parts=None,
         o_parts = torch.empty((S, B, H, Nq, d), dtype=torch.float32, device=q.device)
     if lse_parts is None:
         lse_parts = torch.empty((S, B, H, Nq), dtype=torch.float32, device=q.device)
-    _check_dev(o_parts, "o_parts", (S, B, H, Nq, d), torch.float32)
-    _check_dev(lse_parts, "lse_parts", (S, B, H, Nq), torch.float32)
+    _check_dev(o_parts, "o_parts", (S, B, H, Nq, d), torch.float32, q.device)
+    _check_dev(lse_parts, "lse_parts", (S, B, H, Nq), torch.float32, q.device)
     st = fattn_fwd_partial(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_parts.data_ptr(),
                            lse_parts.data_ptr(), B, H, Nq, Nk, d, float(scale), int(bool(causal)),
                            dtype_code(q), S, _stream(stream))
@@ -395,18 +446,19 @@ def combine(o_parts, lse_parts, dtype=None, out=None, lse=None, stream=None):
     """Merge float32 partials O_s [S, B, H, Nq, d], LSE_s [S, B, H, Nq] into O (``dtype``, default
     float32) and LSE [B, H, Nq]."""
     import torch
-    if o_parts.dim() != 5:
+    _check_dev(o_parts, "o_parts", None, torch.float32)
+    if len(o_parts.shape) != 5:
         raise ValueError("o_parts must be [S, B, H, Nq, d]")
     S, B, H, Nq, d = o_parts.shape
-    _check_dev(o_parts, "o_parts", None, torch.float32)
-    _check_dev(lse_parts, "lse_parts", (S, B, H, Nq), torch.float32)
+    dev = o_parts.device
+    _check_dev(lse_parts, "lse_parts", (S, B, H, Nq), torch.float32, dev)
     dtype = torch.float32 if dtype is None else dtype
     if out is None:
-        out = torch.empty((B, H, Nq, d), dtype=dtype, device=o_parts.device)
+        out = torch.empty((B, H, Nq, d), dtype=dtype, device=dev)
     if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=o_parts.device)
-    _check_dev(out, "out", (B, H, Nq, d))
-    _check_dev(lse, "lse", (B, H, Nq), torch.float32)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    _check_dev(out, "out", (B, H, Nq, d), None, dev)
+    _check_dev(lse, "lse", (B, H, Nq), torch.float32, dev)
     st = fattn_combine(o_parts.data_ptr(), lse_parts.data_ptr(), S, out.data_ptr(), lse.data_ptr(),
                        B, H, Nq, d, dtype_code(out), _stream(stream))
     if st != 0:
@@ -424,16 +476,16 @@ def forward_kouter(q, k, v, causal=False, scale=None, out=None, lse=None, worksp
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     code = dtype_code(q)
-    need = fattn_fwd_kouter_workspace_size(B, H, N, d, code)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, fattn_fwd_kouter_workspace_size(B, H, N, d, code), q.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(out, "out", q)
+    _check_rows(lse, "lse", q)
     st = fattn_fwd_kouter(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                           B, H, N, d, float(scale), int(bool(causal)), code, workspace.data_ptr(),
-                          workspace.numel() * workspace.element_size(), _stream(stream))
+                          _nbytes(workspace), _stream(stream))
     if st != 0:
         raise FattnError(st, "fattn_fwd_kouter")
     return out, lse
@@ -448,13 +500,15 @@ def forward_blocksparse(q, k, v, block_mask, causal=False, scale=None, out=None,
     _check(v, "v", q)
     B, H, N, d = q.shape
     nb = (N + 127) // 128
-    _check_dev(block_mask, "block_mask", (B, H, nb, nb), torch.uint8)
+    _check_dev(block_mask, "block_mask", (B, H, nb, nb), torch.uint8, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(out, "out", q)
+    _check_rows(lse, "lse", q)
     st = fattn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                B, H, N, d, float(scale), int(bool(causal)), dtype_code(q),
                                block_mask.data_ptr(), _stream(stream))
@@ -464,26 +518,22 @@ def forward_blocksparse(q, k, v, block_mask, causal=False, scale=None, out=None,
 
 
 def backward_blocksparse(q, k, v, o, do, lse, block_mask, causal=False, scale=None, workspace=None,
-                         stream=None):
+                         stream=None, dq=None, dk=None, dv=None):
     """dQ, dK, dV of block-sparse attention (the same ``block_mask`` as forward_blocksparse)."""
     import torch
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
-        _check(t, n, q if n != "q" else None)
+    _check_bwd_inputs(q, k, v, o, do, lse)
     B, H, N, d = q.shape
     nb = (N + 127) // 128
-    _check_dev(block_mask, "block_mask", (B, H, nb, nb), torch.uint8)
+    _check_dev(block_mask, "block_mask", (B, H, nb, nb), torch.uint8, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     code = dtype_code(q)
-    need = fattn_bwd_workspace_size(B, H, N, d, code)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    workspace = _workspace(workspace, fattn_bwd_workspace_size(B, H, N, d, code), q.device)
+    dq, dk, dv = _grad_outputs(q, dq, dk, dv)
     st = fattn_bwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                B, H, N, d, float(scale), int(bool(causal)), code, block_mask.data_ptr(),
-                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                               _stream(stream))
+                               workspace.data_ptr(), _nbytes(workspace), _stream(stream))
     if st != 0:
         raise FattnError(st, "fattn_bwd_blocksparse")
     return dq, dk, dv

@@ -1,7 +1,9 @@
-"""Build libfattn.so (and the issue-rate micro-benchmark) for gfx950 with hipcc (no GPU needed:
-hipcc cross-compiles).
+"""Build libfattn.so for gfx950 with hipcc (no GPU needed: hipcc cross-compiles).
 
-Usage: python -m io_aware_tiled_fattn_amd.build [--verbose] [--resource-usage]
+Usage: python -m io_aware_tiled_fattn_amd.build [--verbose] [--resource-usage] [--tools]
+
+--tools also builds the stand-alone measurement programs under microbench/ (not part of the
+library; each writes its own executable beside its source).
 """
 from __future__ import annotations
 
@@ -53,11 +55,13 @@ def _compile(src, hipcc, extra, verbose):
     return obj, text
 
 
-TOOLS = {"issue_rates.hip": os.path.join(HERE, "issue_rates")}  # stand-alone measurement programs
+MICROBENCH = os.path.join(HERE, "microbench")
+TOOLS = ["issue_rates.hip", "atomic_rates.hip"]  # stand-alone measurement programs, on request
 
 
-def _build_tool(src, exe, hipcc, verbose):
-    cmd = [hipcc, *[c for c in COMMON if c != "-fPIC"], os.path.join(CSRC, src), "-o", exe + ".tmp"]
+def _build_tool(src, hipcc, verbose):
+    exe = os.path.join(MICROBENCH, os.path.splitext(src)[0])
+    cmd = [hipcc, *[c for c in COMMON if c != "-fPIC"], os.path.join(MICROBENCH, src), "-o", exe + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -66,7 +70,7 @@ def _build_tool(src, exe, hipcc, verbose):
     os.replace(exe + ".tmp", exe)
 
 
-def build(verbose: bool = False, resource_usage: bool = False) -> str:
+def build(verbose: bool = False, resource_usage: bool = False, tools: bool = False) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
@@ -81,8 +85,10 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, OUT)
-    for src, exe in TOOLS.items():
-        _build_tool(src, exe, hipcc, verbose)
+    if tools:
+        for src in TOOLS:
+            if os.path.exists(os.path.join(MICROBENCH, src)):
+                _build_tool(src, hipcc, verbose)
     return OUT
 
 
@@ -90,8 +96,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--resource-usage", action="store_true")
+    ap.add_argument("--tools", action="store_true", help="also build the microbench/ programs")
     a = ap.parse_args(argv)
-    print(build(a.verbose, a.resource_usage))
+    print(build(a.verbose, a.resource_usage, a.tools))
 
 
 if __name__ == "__main__":

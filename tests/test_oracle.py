@@ -491,3 +491,78 @@ def test_loop_order_bytes_closed_forms():
     qc = traffic.loop_order_bytes(N, d, 128, 128, "q_outer", causal=True)
     nb = N // 128
     assert qc == 2 * N * d * s + 4 * N + 2 * 128 * d * s * (nb * (nb + 1) // 2)
+
+
+# --------------------------------------------------------------------------------------------
+# Whole-tensor wrappers and the causal traffic branch
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiled_forward_over_batch_and_heads_matches_the_definition(causal):
+    # [B, H, N, d] with every (b, h) slice drawn differently (and scaled differently), so a
+    # swapped or repeated batch/head index in the wrapper shows up as a large error
+    B, H, N, d = 2, 3, 37, 8
+    r = _rng(81, int(causal))
+    q, k, v = (r.standard_normal((B, H, N, d)) for _ in range(3))
+    for b in range(B):
+        for h in range(H):
+            q[b, h] *= 1 + b + 2 * h
+            v[b, h] += 10 * (b * H + h)
+    o_ref, lse_ref = att.forward(q, k, v, 0.3, causal)
+    o, lse = tiled.forward(q, k, v, 0.3, 16, 5, causal)
+    assert o.shape == (B, H, N, d) and lse.shape == (B, H, N)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-11)
+    # each output slice depends on its own input slice only: permuting the heads permutes them
+    perm = [2, 0, 1]
+    o_p, lse_p = tiled.forward(q[:, perm], k[:, perm], v[:, perm], 0.3, 16, 5, causal)
+    np.testing.assert_array_equal(o_p, o[:, perm])
+    np.testing.assert_array_equal(lse_p, lse[:, perm])
+
+
+def test_tiled_bytes_with_rereads_causal_closed_form():
+    s = 2
+    # N a multiple of Br: query block i re-reads the K/V prefix of (i + 1) Br keys, so the K/V
+    # reads sum to Br d s nb (nb + 1) (an arithmetic series), plus Q and O once and 4 B of LSE
+    for N, d, Br in ((4096, 128, 128), (4096, 128, 256), (1024, 64, 64)):
+        nb = N // Br
+        got = traffic.tiled_bytes_with_rereads(N, d, Br, s, causal=True)
+        assert got == 2 * N * d * s + 4 * N + Br * d * s * nb * (nb + 1)
+        # about half the non-causal re-reads for many blocks
+        full = traffic.tiled_bytes_with_rereads(N, d, Br, s)
+        kv_c, kv_f = got - 2 * N * d * s - 4 * N, full - 2 * N * d * s - 4 * N
+        assert kv_c / kv_f == pytest.approx((nb + 1) / (2 * nb), rel=1e-12)
+    # ragged N: the last block's prefix is capped at N keys
+    N, d, Br = 1000, 64, 128
+    nb = math.ceil(N / Br)
+    kv = sum(2 * min(N, (i + 1) * Br) * d * s for i in range(nb))
+    assert kv == 2 * d * s * (128 * (nb - 1) * nb // 2 + N)
+    assert traffic.tiled_bytes_with_rereads(N, d, Br, s, causal=True) == 2 * N * d * s + 4 * N + kv
+    # when Bc divides Br, the causal Q-outer visits of the loop-order model read exactly the same
+    # key prefix for every query block, so both models agree
+    for N, Br, Bc in ((4096, 128, 64), (4096, 256, 128), (1000, 128, 64), (1000, 128, 32), (77, 16, 16)):
+        assert traffic.tiled_bytes_with_rereads(N, 64, Br, s, causal=True) == \
+            traffic.loop_order_bytes(N, 64, Br, Bc, "q_outer", causal=True, elem_bytes=s)
+    # one query block: no re-reads at all, causal or not
+    assert traffic.tiled_bytes_with_rereads(100, 64, 128, s, causal=True) == \
+        traffic.tiled_bytes_with_rereads(100, 64, 128, s) == 4 * 100 * 64 * s + 4 * 100
+
+
+def test_max_rel_floor_binds_only_below_it():
+    from oracle import metrics as M
+    r = np.zeros((2, 3, 4))
+    r[0] = 2.0            # slice 0: exact values of magnitude 2
+    x = r.copy()
+    x[0, 0, 0] += 0.01    # slice 0 error 0.01 -> 0.005 relative, whatever the floor below 2
+    x[1, 1, 1] = 1e-6     # slice 1: exact zero, rounding noise 1e-6
+    assert M.max_rel(x[:1], r[:1]) == pytest.approx(0.005, rel=1e-12)
+    assert M.max_rel(x[:1], r[:1], floor=1.0) == pytest.approx(0.005, rel=1e-12)
+    # the zero slice alone: infinite without a floor, noise / floor with one
+    assert M.max_rel(x[1:], r[1:]) == np.inf
+    assert M.max_rel(x[1:], r[1:], floor=1e-3) == pytest.approx(1e-3, rel=1e-9)
+    # both slices: the worse of the two
+    assert M.max_rel(x, r, floor=1e-3) == pytest.approx(0.005, rel=1e-12)
+    # identical zero slices are exact
+    assert M.max_rel(r[1:], r[1:]) == 0.0
+    # a floor above a slice's own scale replaces its denominator
+    assert M.max_rel(x[:1], r[:1], floor=4.0) == pytest.approx(0.0025, rel=1e-12)
