@@ -240,11 +240,15 @@ def _check(t, name, like=None):
         _check_dev(t, name, like.shape, like.dtype, like.device)
 
 
-def _check_rows(t, name, q, n=None):
-    """A float32 [B, H, N] per-row tensor (LSE, D) for q [B, H, N, d]."""
+def _check_rows(t, name, q, flat_ok=False):
+    """A float32 [B, H, N] per-row tensor (LSE, D) for q [B, H, N, d]; with ``flat_ok`` a
+    contiguous [B * H * N] vector is accepted as well."""
     import torch
     B, H, N, _ = q.shape
-    _check_dev(t, name, (B, H, N if n is None else n), torch.float32, q.device)
+    if flat_ok and t is not None and len(t.shape) == 1:
+        _check_dev(t, name, (B * H * N,), torch.float32, q.device)
+    else:
+        _check_dev(t, name, (B, H, N), torch.float32, q.device)
 
 
 def _nbytes(t) -> int:
@@ -356,11 +360,11 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, stre
 def backward_stages(q, k, v, o, do, lse, dq, dk, dv, dvec, causal=False, scale=None, stream=None,
                     stages=(0, 1, 2)):
     """Run the chosen stages of the backward (0: D = rowsum(dO*O), 1: dK/dV, 2: dQ) into
-    preallocated outputs; ``dvec`` is a float32 [B, H, N] device tensor."""
+    preallocated outputs; ``dvec`` is a float32 [B, H, N] (or flat [B * H * N]) device tensor."""
     _check_bwd_inputs(q, k, v, o, do, lse)
     for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         _check(t, n, q)
-    _check_rows(dvec, "dvec", q)
+    _check_rows(dvec, "dvec", q, flat_ok=True)
     for stage in stages:
         if stage not in (0, 1, 2):
             raise ValueError(f"unknown backward stage {stage}")

@@ -755,9 +755,9 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
 
   const bool big = (size_t)r.N * D * 2 >= ((size_t)1 << 31);
   a.bh_total = (int)BH;
-  a.hgroup = head_group(a.bh_total);
   auto dkdv = [&]() {
     a.ntiles = (r.N + PairCfg<D>::BKV - 1) / PairCfg<D>::BKV;
+    a.hgroup = head_group(a.bh_total, (size_t)2 * r.N * D * 2);
     dim3 gp((unsigned)(BH * a.ntiles));
     auto gop = [&](auto kern) { hipLaunchKernelGGL(kern, gp, dim3(PairCfg<D>::NT), 0, st, a); };
     if (r.causal)
@@ -769,6 +769,7 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
   auto dq = [&](auto with_d) {
     constexpr bool WD = decltype(with_d)::value;
     a.ntiles = (r.N + DqCfg<D>::BQ - 1) / DqCfg<D>::BQ;
+    a.hgroup = head_group(a.bh_total, (size_t)2 * r.N * D * 2);
     dim3 g2((unsigned)(BH * a.ntiles));
     auto go = [&](auto kern) { hipLaunchKernelGGL(kern, g2, dim3(DqCfg<D>::NT), 0, st, a); };
     if (r.causal)

@@ -29,9 +29,10 @@
 //    exactly 1 for almost every tile (page 2, tips), the exp2 arguments stay <= 8, and the result
 //    is unchanged because O and l always share the same reference max.
 //  * Work-group order: the 8 XCDs each take a contiguous range of heads; with the causal mask an
-//    XCD takes its heads four at a time and runs their query tiles longest first (the group's
-//    last tiles, then the ones before), which balances the triangular work across CUs while only
-//    four heads' K/V compete for the XCD's L2.
+//    XCD takes its heads a few at a time (four, or fewer once their K/V pass 8 MiB) and runs
+//    their query tiles longest first (the group's last tiles, then the ones before), which
+//    balances the triangular work across CUs while only those heads' K/V compete for the XCD's
+//    L2.
 #include "fattn_device.hpp"
 #include "fattn_launch.hpp"
 
@@ -624,7 +625,7 @@ hipError_t launch16(const FwdReq& r, hipStream_t st) {
   a.N = r.N;
   a.n_qtiles = (r.N + BR - 1) / BR;
   a.bh_total = r.B * r.H;
-  a.hgroup = head_group(a.bh_total);
+  a.hgroup = head_group(a.bh_total, (size_t)2 * r.N * D * 2);
   a.c = r.scale == 0.f ? 1.f : fabsf(r.scale) * kLog2e;
   a.neg_mask = r.scale < 0.f ? 0x80008000u : 0u;
   a.keep_mask = r.scale == 0.f ? 0u : 0xffffffffu;

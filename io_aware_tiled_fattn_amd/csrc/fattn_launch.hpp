@@ -83,13 +83,22 @@ int splitkv_split_len(int Nk, int num_splits);
 hipError_t launch_splitkv_partial(const SplitReq& r, hipStream_t stream);
 hipError_t launch_combine(const CombineReq& r, hipStream_t stream);
 
-// Causal grid order (causal_xcd_order): each XCD takes its heads four at a time. Measured on
+// Causal grid order (causal_xcd_order): how many heads an XCD works on at once. Measured on
 // MI355X at N = 4096, d = 128 against all of an XCD's heads at once: equal at 4 heads per XCD,
-// forward +1.3% at 8, forward +4% and backward +6% at 16 (fewer heads' K/V competing for the
-// XCD's L2); one head at a time loses the balance across the causal triangle (up to -26%).
-inline int head_group(int bh_total) {
+// forward +1.3% at 8, forward +4% and backward +6% at 16 (fewer heads' streamed tiles competing
+// for the XCD's 4 MiB L2); one head at a time loses the balance across the causal triangle
+// (up to -26%) when a head has fewer tiles than the XCD has CUs. So a group holds four heads,
+// or fewer once their streamed tensors pass 8 MiB (`stream_bytes`: K and V per head in the
+// forward and dQ kernels, Q and dO in the dK/dV kernel; 2 MiB at N = 4096, d = 128, 8 MiB at
+// N = 16384, where one head is a group). Wherever the budget shrinks the group, a head has at
+// least 32 tiles, so a group still gives each of an XCD's 32 CUs two or more.
+inline int head_group(int bh_total, size_t stream_bytes) {
   const int hpx = bh_total / 8;
-  return hpx < 1 ? 1 : (hpx < 4 ? hpx : 4);
+  if (hpx <= 1) return 1;
+  const size_t budget = (size_t)8 << 20;
+  int g = stream_bytes > 0 ? (int)(budget / stream_bytes) : 4;
+  g = g < 1 ? 1 : (g > 4 ? 4 : g);
+  return g > hpx ? hpx : g;
 }
 
 // K-outer (FA-1 order) forward, an ablation: one launch per key/value block.

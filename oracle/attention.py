@@ -42,13 +42,14 @@ def _as64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _masked_scores(q_rows, k, scale, causal, row0):
-    """Scaled logits for query rows row0.. (one (b, h) slice), -inf above the diagonal if causal."""
+def _masked_scores(q_rows, k, scale, causal, row0, causal_offset=0):
+    """Scaled logits for query rows row0.. (one (b, h) slice); with ``causal``, -inf where key
+    j > row + causal_offset."""
     s = (q_rows @ k.T) * scale
     if causal:
         rows = np.arange(row0, row0 + q_rows.shape[0])[:, None]
         cols = np.arange(k.shape[0])[None, :]
-        s[cols > rows] = -np.inf
+        s[cols > rows + causal_offset] = -np.inf
     return s
 
 
@@ -94,17 +95,18 @@ def forward(q, k, v, scale, causal=False, rows=None, heads=None, causal_offset=0
     return o, lse
 
 
-def backward_slice(q, k, v, do, scale, causal=False, chunk=_CHUNK):
-    """dQ, dK, dV (float64) for one (b, h) slice, recomputing O and LSE from the definition."""
+def backward_slice(q, k, v, do, scale, causal=False, chunk=_CHUNK, causal_offset=0):
+    """dQ [Nq, d], dK, dV [Nk, d] (float64) for one (b, h) slice, recomputing O and LSE from the
+    definition; with ``causal``, query i sees keys j <= i + causal_offset (as in forward_slice)."""
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
-    o, lse = forward_slice(q, k, v, scale, causal, chunk=chunk)
+    o, lse = forward_slice(q, k, v, scale, causal, chunk=chunk, causal_offset=causal_offset)
     dq = np.empty_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     dvec = np.sum(do * o, axis=1)
     for r0 in range(0, q.shape[0], chunk):
         r1 = min(q.shape[0], r0 + chunk)
-        s = _masked_scores(q[r0:r1], k, scale, causal, r0)
+        s = _masked_scores(q[r0:r1], k, scale, causal, r0, causal_offset)
         p = np.exp(s - lse[r0:r1, None])
         dv += p.T @ do[r0:r1]
         dp = do[r0:r1] @ v.T

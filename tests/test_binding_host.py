@@ -183,3 +183,12 @@ def test_other_wrappers_check_their_outputs(calls):
     fa.forward_splitkv(_t((B, H, 4, d)), _t(), _t(), out=_t((B, H, 4, d)), lse=Dev((B, H, 4), torch.float32),
                        workspace=Dev((1024,), torch.uint8), stream=Stream())
     assert calls == ["fattn_fwd_kouter", "fattn_fwd_blocksparse", "fattn_fwd_splitkv"]
+
+
+def test_backward_stages_accepts_a_flat_dvec(calls):
+    fa.backward_stages(_t(), _t(), _t(), _t(), _t(), _lse(), _t(), _t(), _t(), Dev((B * H * N,), torch.float32),
+                       stream=Stream(), stages=(0,))
+    with pytest.raises(ValueError, match="dvec"):
+        fa.backward_stages(_t(), _t(), _t(), _t(), _t(), _lse(), _t(), _t(), _t(),
+                           Dev((B * H * N - 1,), torch.float32), stream=Stream())
+    assert calls == ["fattn_bwd_preprocess"]

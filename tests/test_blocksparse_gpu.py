@@ -9,7 +9,7 @@ import pytest
 import fattn_inputs as fi
 from oracle import blocksparse as obs
 from oracle import metrics as M
-from tests.gpu_util import from_dev, log, sample_heads, upload
+from tests.gpu_util import from_dev, log, spread_heads, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -90,14 +90,14 @@ def test_blocksparse_empty_mask_and_single_block():
     _check(from_dev(o), from_dev(lse), o_ref, lse_ref, "bf16")
 
 
-def test_blocksparse_workload5_shape_sampled_heads():
+def test_blocksparse_workload5_shape_spread_heads():
     w = fi.WORKLOADS[5]
     inp = fi.workload_inputs(5, with_do=False)
     nb = w.N // 128
     mask = fi.block_mask(w.B, w.H, nb, 0.25, 5)
     log("blocksparse B=2 H=16 N=4096 d=128 causal, density 0.25 + diagonal")
     o, lse = _run(inp, mask, True)
-    heads = sample_heads(w.B, w.H)
+    heads = spread_heads(w.B, w.H, 8)
     o_ref, lse_ref = obs.forward(inp.q, inp.k, inp.v, w.scale, mask, True, heads=heads)
     for b, h in heads:
         _check(o[b, h], lse[b, h], o_ref[b, h], lse_ref[b, h], "bf16")
@@ -184,14 +184,14 @@ def test_blocksparse_backward_empty_mask_and_single_block():
     assert np.all(dk[0, 0, :128] == 0) and np.all(dk[0, 0, 256:] == 0)
 
 
-def test_blocksparse_backward_workload5_shape_sampled_heads():
+def test_blocksparse_backward_workload5_shape_spread_heads():
     w = fi.WORKLOADS[5]
     inp = fi.workload_inputs(5)
     nb = w.N // 128
     mask = fi.block_mask(w.B, w.H, nb, 0.25, 5)
     log("blocksparse bwd B=2 H=16 N=4096 d=128 causal, density 0.25 + diagonal")
     dq, dk, dv, _ = _run_bwd(inp, mask, True)
-    heads = sample_heads(w.B, w.H)
+    heads = spread_heads(w.B, w.H, 8)
     ref = obs.backward(inp.q, inp.k, inp.v, inp.do, w.scale, mask, True, heads=heads)
     for b, h in heads:
         _check_grads((dq[b, h], dk[b, h], dv[b, h]), tuple(r[b, h] for r in ref), "bf16")

@@ -14,7 +14,8 @@ import pytest
 import fattn_inputs as fi
 from oracle import attention as att
 from oracle import metrics as M
-from tests.gpu_util import from_dev, log, sample_heads, upload
+from tests.gpu_util import Guarded, every_head, from_dev, log, upload
+from tests.periodic import block_problem as _block_problem
 
 pytestmark = pytest.mark.gpu
 
@@ -92,15 +93,16 @@ def _workload5():
     return fi.workload_inputs(5)
 
 
-def test_workload5_backward_sampled_heads():
+def test_workload5_backward_every_head():
+    # every (b, h) slice of dQ, dK and dV compared element by element with the oracle
     w = fi.WORKLOADS[5]
     inp = _workload5()
     got = _run(inp, True)
-    heads = sample_heads(w.B, w.H, 3)
+    heads = every_head(w.B, w.H)
     ref = att.backward(inp.q, inp.k, inp.v, inp.do, w.scale, True, heads=heads)
-    for b, h in heads:
-        log(f"  head ({b},{h})")
-        _check(tuple(g[b, h] for g in got), tuple(r[b, h] for r in ref), "bf16")
+    for name, x, r in zip(("dQ", "dK", "dV"), got, ref):
+        log(f"    {name}: max-rel over {len(heads)} heads {M.max_rel(x, r):.3e}, rel-l2 {M.rel_l2(x, r):.3e}")
+    _check(got, ref, "bf16")
 
 
 def test_workload5_gradient_identities_every_head():
@@ -167,3 +169,60 @@ def test_backward_stage_entry_points_match_fattn_bwd(causal, N):
     torch.cuda.synchronize()
     for x, y in zip((dq, dk, dv), ref):
         assert torch.equal(x, y)
+
+
+# --------------------------------------------------------------------------------------------
+# A head of 2 GiB or more: the backward's 64-bit address path
+
+
+@pytest.mark.timeout(900)
+def test_backward_huge_head_uses_64bit_addressing():
+    # One causal bf16 head of N = 64 R + 37 rows (Q, K, V, dO repeat one 64-row block), so that
+    # N d 2 >= 2^31 bytes: the dK/dV and dQ kernels take 64-bit addresses, with a ragged last
+    # tile. Exact gradients follow from small oracle problems (_block_problem): dQ for every row
+    # of blocks 0, 1, R/2, R-1 and the tail, dK and dV for every key of the last two blocks (keys
+    # of block c are seen by query blocks c .. R, so only blocks R-1 and R contribute there).
+    import torch
+    fa = _fa()
+    d, t = 128, 37
+    R = (1 << 23) // 64 + 1
+    N = 64 * R + t
+    assert N * d * 2 >= 1 << 31
+    scale = 1 / math.sqrt(d)
+    blk = fi.make_inputs((1, 1, 64, d), "bf16", 678, with_do=True)
+    qb, kb, vb, dob = upload(blk)
+    reps = lambda x: torch.cat([x[0, 0].repeat(R, 1), x[0, 0, :t]]).reshape(1, 1, N, d)
+    q, k, v, do = reps(qb), reps(kb), reps(vb), reps(dob)
+    log(f"backward huge head N={N}: forward")
+    o, lse = fa.forward(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    log("  backward")
+    gq, gk, gv = (Guarded((1, 1, N, d), torch.bfloat16) for _ in range(3))
+    fa.backward(q, k, v, o, do, lse, causal=True, dq=gq.t, dk=gk.t, dv=gv.t)
+    torch.cuda.synchronize()
+    log("  checks")
+    for g, name in ((gq, "dQ"), (gk, "dK"), (gv, "dV")):
+        g.check(name=name)
+    # exact identities over the whole head: sum_j dK_j = 0, sum_j dV_j = sum_i dO_i
+    dk_sum = gk.t[0, 0].double().sum(0)
+    dv_sum = gv.t[0, 0].double().sum(0) - do[0, 0].double().sum(0)
+    bk = 2.0 ** -6 * gk.t[0, 0].double().abs().sum(0) + 1e-3
+    bv = 2.0 ** -6 * (gv.t[0, 0].double().abs().sum(0) + do[0, 0].double().abs().sum(0)) + 1e-3
+    assert bool((dk_sum.abs() <= bk).all()) and bool((dv_sum.abs() <= bv).all())
+    q64, k64, v64, do64 = (x[0, 0].astype(np.float64) for x in (blk.q, blk.k, blk.v, blk.do))
+    rows = lambda g, c, n: from_dev(g.t[0, 0, 64 * c: 64 * c + n])
+    ref_q, got_q = [], []
+    for c in (0, 1, R // 2, R - 1, R):
+        nr = 64 if c < R else t
+        ref_q.append(_block_problem(q64, k64, v64, do64, scale, c, nr)[0])
+        got_q.append(rows(gq, c, nr))
+    # keys of block R - 1: its own query block (diagonal part) and the tail block (folded keys)
+    _, _, _, dk_own, dv_own = _block_problem(q64, k64, v64, do64, scale, R - 1, 64)
+    _, dk_fold, dv_fold, dk_tail, dv_tail = _block_problem(q64, k64, v64, do64, scale, R, t)
+    ref_k = np.concatenate([dk_own + dk_fold, dk_tail])
+    ref_v = np.concatenate([dv_own + dv_fold, dv_tail])
+    got_k = np.concatenate([rows(gk, R - 1, 64), rows(gk, R, t)])
+    got_v = np.concatenate([rows(gv, R - 1, 64), rows(gv, R, t)])
+    got = (np.concatenate(got_q)[None], got_k[None], got_v[None])
+    ref = (np.concatenate(ref_q)[None], ref_k[None], ref_v[None])
+    _check(got, ref, "bf16")

@@ -14,7 +14,7 @@ import pytest
 import fattn_inputs as fi
 from oracle import dropout as odr
 from oracle import metrics as M
-from tests.gpu_util import from_dev, log, sample_heads, to_dev, upload
+from tests.gpu_util import from_dev, log, spread_heads, to_dev, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -113,13 +113,13 @@ def _workload5():
     return fi.workload_inputs(5)
 
 
-def test_dropout_workload5_sampled_heads():
+def test_dropout_workload5_spread_heads():
     w = fi.WORKLOADS[5]
     inp = _workload5()
     p, seed = 0.1, 20261202
     log("dropout workload 5 (B=2 H=16 N=4096 d=128 causal, p=0.1)")
     o, lse, dq, dk, dv = _run(inp, True, p, seed)
-    heads = sample_heads(w.B, w.H)
+    heads = spread_heads(w.B, w.H, 8)
     o_ref, lse_ref = odr.forward(inp.q, inp.k, inp.v, w.scale, True, p, seed, heads=heads)
     ref = odr.backward(inp.q, inp.k, inp.v, inp.do, w.scale, True, p, seed, heads=heads)
     for b, h in heads:

@@ -14,7 +14,7 @@ import fattn_inputs as fi
 from oracle import attention as att
 from oracle import metrics as M
 from oracle import splitkv as osk
-from tests.gpu_util import from_dev, log, sample_heads, to_dev, upload
+from tests.gpu_util import Guarded, every_head, from_dev, log, sample_heads, spread_heads, to_dev, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -26,12 +26,13 @@ def _fa():
     return fa
 
 
-def _check(o, lse, o_ref, lse_ref, dtype, lse_tol=None, o_abs_factor=1.0):
+def _check(o, lse, o_ref, lse_ref, dtype, lse_tol=None, o_abs_factor=1.0, quiet=False):
     tol = M.TOL[dtype]
     ea = M.max_abs(o, o_ref)
     er = M.max_rel(o, o_ref)
     el = M.max_abs(lse, lse_ref)
-    log(f"    O max-abs {ea:.3e} max-rel {er:.3e}  LSE max-abs {el:.3e}")
+    if not quiet:
+        log(f"    O max-abs {ea:.3e} max-rel {er:.3e}  LSE max-abs {el:.3e}")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     assert ea <= tol["o_abs"] * o_abs_factor, ea
     if tol["o_rel"] is not None:
@@ -187,31 +188,46 @@ def _workload(ident):
     return fi.workload_inputs(ident, with_do=False)
 
 
-def _workload_heads(ident, causal, Br=0, Bc=0):
+@functools.lru_cache(maxsize=2)
+def _workload_ref(ident, causal, heads):
+    w = fi.WORKLOADS[ident]
+    inp = _workload(ident)
+    return att.forward(inp.q, inp.k, inp.v, w.scale, causal, heads=list(heads))
+
+
+def _workload_heads(ident, causal, Br=0, Bc=0, heads=None):
+    """Run a full-size workload and compare the given heads (default: every head) element by
+    element with the oracle."""
     w = fi.WORKLOADS[ident]
     inp = _workload(ident)
     o, lse = _run(inp, causal, Br=Br, Bc=Bc)
-    heads = sample_heads(w.B, w.H, 2 if w.N > 8192 else 3)
-    o_ref, lse_ref = att.forward(inp.q, inp.k, inp.v, w.scale, causal, heads=heads)
+    heads = tuple(every_head(w.B, w.H) if heads is None else heads)
+    o_ref, lse_ref = _workload_ref(ident, causal, heads)
+    worst = [0.0, 0.0]
     for b, h in heads:
-        log(f"  head ({b},{h})")
-        _check(o[b, h], lse[b, h], o_ref[b, h], lse_ref[b, h], w.dtype)
+        worst[0] = max(worst[0], M.max_abs(o[b, h], o_ref[b, h]))
+        worst[1] = max(worst[1], M.max_abs(lse[b, h], lse_ref[b, h]))
+        _check(o[b, h], lse[b, h], o_ref[b, h], lse_ref[b, h], w.dtype, quiet=True)
+    log(f"  {len(heads)} heads: O max-abs {worst[0]:.3e}, LSE max-abs {worst[1]:.3e}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     return inp, o, lse
 
 
 @pytest.mark.parametrize("tile", [(0, 0), (64, 64), (64, 128), (128, 64), (128, 128), (256, 64), (256, 128)])
-def test_workload3_bf16_causal_tiles(tile):
-    log(f"workload 3 tile {tile}")
+def test_workload3_bf16_causal_tiles_every_head(tile):
+    log(f"workload 3 tile {tile}, every head")
     _workload_heads(3, True, *tile)
 
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_workload4_bf16_long(causal):
+    # one head from each XCD's range of heads, each compared element by element
+    w = fi.WORKLOADS[4]
     log(f"workload 4 causal={causal}")
-    _workload_heads(4, causal)
+    _workload_heads(4, causal, heads=spread_heads(w.B, w.H, 8))
 
 
-def test_workload5_forward():
+def test_workload5_forward_every_head():
     _workload_heads(5, True)
 
 
@@ -341,8 +357,11 @@ def test_forward_huge_head_uses_64bit_addressing():
     qb, kb, vb, _ = upload(blk)
     reps = lambda x: torch.cat([x[0, 0].repeat(R, 1), x[0, 0, :37]]).reshape(1, 1, N, d)
     q, k, v = reps(qb), reps(kb), reps(vb)
-    o, lse = fa.forward(q, k, v, causal=True)
+    go, gl = Guarded((1, 1, N, d), torch.bfloat16), Guarded((1, 1, N), torch.float32)
+    o, lse = fa.forward(q, k, v, causal=True, out=go.t, lse=gl.t)
     torch.cuda.synchronize()
+    go.check(name="O")
+    gl.check(name="LSE")
     rows = [0, 37, 63, 64, 1000, N // 2, N - 38, N - 2, N - 1]
     o = from_dev(o[0, 0, rows])
     lse = from_dev(lse[0, 0, rows])

@@ -339,8 +339,8 @@ def test_tiled_model_block_with_only_masked_keys():
 # Gradients
 
 
-def _loss(q, k, v, do, scale, causal):
-    o, _ = att.forward_slice(q, k, v, scale, causal)
+def _loss(q, k, v, do, scale, causal, causal_offset=0):
+    o, _ = att.forward_slice(q, k, v, scale, causal, causal_offset=causal_offset)
     return float(np.sum(do * o))
 
 
@@ -566,3 +566,56 @@ def test_max_rel_floor_binds_only_below_it():
     assert M.max_rel(r[1:], r[1:]) == 0.0
     # a floor above a slice's own scale replaces its denominator
     assert M.max_rel(x[:1], r[:1], floor=4.0) == pytest.approx(0.0025, rel=1e-12)
+
+
+@pytest.mark.parametrize("Nq,Nk,offset", [(1, 5, 4), (3, 7, 4), (4, 4, 2), (5, 9, 6), (2, 6, 0)])
+def test_gradients_with_a_causal_offset_match_finite_differences(Nq, Nk, offset):
+    # queries are the last positions of a longer key sequence (query i sees keys j <= i + offset)
+    r = _rng(24, Nq, Nk, offset)
+    d, scale = 3, 0.7
+    q, do = r.standard_normal((Nq, d)), r.standard_normal((Nq, d))
+    k, v = r.standard_normal((Nk, d)), r.standard_normal((Nk, d))
+    dq, dk, dv = att.backward_slice(q, k, v, do, scale, True, causal_offset=offset)
+    assert dq.shape == (Nq, d) and dk.shape == dv.shape == (Nk, d)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            a = {"q": q, "k": k, "v": v}
+            b = {"q": q, "k": k, "v": v}
+            a[name], b[name] = x.copy(), x.copy()
+            a[name][idx] += eps
+            b[name][idx] -= eps
+            num[idx] = (_loss(a["q"], a["k"], a["v"], do, scale, True, offset)
+                        - _loss(b["q"], b["k"], b["v"], do, scale, True, offset)) / (2 * eps)
+        den = max(1.0, float(np.max(np.abs(num))))
+        assert float(np.max(np.abs(num - g))) / den < 1e-7, name
+    # keys no query can see get no gradient
+    hidden = np.arange(Nk) > Nq - 1 + offset
+    assert np.all(dk[hidden] == 0) and np.all(dv[hidden] == 0)
+
+
+def test_periodic_block_problem_equals_the_explicit_head():
+    # the folding used by the 2 GiB backward test, on a head small enough to build explicitly:
+    # 3 whole copies of a 64-row block plus a 5-row tail
+    from tests.periodic import block_problem
+    d, R, t, scale = 8, 3, 5, 0.6
+    r = _rng(25)
+    q, k, v, do = (r.standard_normal((64, d)) for _ in range(4))
+    rep = lambda x: np.concatenate([np.tile(x, (R, 1)), x[:t]])
+    dq, dk, dv = att.backward_slice(rep(q), rep(k), rep(v), rep(do), scale, True)
+    for c in range(R + 1):
+        nr = 64 if c < R else t
+        got = block_problem(q, k, v, do, scale, c, nr)
+        np.testing.assert_allclose(got[0], dq[64 * c: 64 * c + nr], rtol=0, atol=1e-11)
+    # keys of block c collect their own block's part and one folded part per later block
+    for c in range(R + 1):
+        nr = 64 if c < R else t
+        _, _, _, dk_own, dv_own = block_problem(q, k, v, do, scale, c, nr)
+        ek, ev = dk_own.copy(), dv_own.copy()
+        for b in range(c + 1, R + 1):
+            _, dk_f, dv_f, _, _ = block_problem(q, k, v, do, scale, b, 64 if b < R else t)
+            ek += dk_f[:nr]
+            ev += dv_f[:nr]
+        np.testing.assert_allclose(ek, dk[64 * c: 64 * c + nr], rtol=0, atol=1e-11)
+        np.testing.assert_allclose(ev, dv[64 * c: 64 * c + nr], rtol=0, atol=1e-11)

@@ -14,7 +14,7 @@ import fattn_inputs as fi
 from oracle import attention as att
 from oracle import metrics as M
 from oracle import splitkv as osk
-from tests.gpu_util import from_dev, log, sample_heads, to_dev
+from tests.gpu_util import from_dev, log, spread_heads, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -182,12 +182,12 @@ def test_splitkv_plus_500_shift_stays_finite(dtype):
 
 
 # --------------------------------------------------------------------------------------------
-# Full-size decode workloads: sampled heads against the oracle
+# Full-size decode workloads: one head from every XCD's head range against the oracle
 
 
 @pytest.mark.parametrize("ident", sorted(fi.DECODE_WORKLOADS))
 @pytest.mark.parametrize("causal", [False, True])
-def test_decode_workloads_sampled_heads(ident, causal):
+def test_decode_workloads_spread_heads(ident, causal):
     fa = _fa()
     w = fi.DECODE_WORKLOADS[ident]
     log(f"decode workload {ident} ({w.name}) causal={causal}")
@@ -196,7 +196,7 @@ def test_decode_workloads_sampled_heads(ident, causal):
     o, lse = fa.forward_splitkv(q, k, v, causal=causal)
     _torch().cuda.synchronize()
     o, lse = from_dev(o), from_dev(lse)
-    heads = sample_heads(w.B, w.H, 4) + [(1, 7)]
+    heads = spread_heads(w.B, w.H, 8) + [(1, 7)]
     o_ref, lse_ref = att.forward(inp.q, inp.k, inp.v, w.scale, causal, heads=heads,
                                  causal_offset=w.Nk - w.Nq)
     for b, h in heads:
