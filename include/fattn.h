@@ -20,7 +20,8 @@
  *  - Tensors are dense, contiguous [B, H, N, d] with d innermost, in the element type `dtype`.
  *    LSE (and the workspace's D vector) is float32 [B, H, N].
  *  - Every pointer is a caller-owned DEVICE pointer on the current HIP device, 16-byte aligned.
- *    The library allocates nothing, keeps no global mutable state and is re-entrant.
+ *    The library allocates nothing and is re-entrant; its only state is the static device
+ *    buffer of fattn_bwd_noalloc (below), which that entry point alone uses.
  *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream). Work is enqueued
  *    on it and the call returns at once; the caller synchronises.
  *  - Arguments are checked on the host before any HIP call: a call that returns an error has
@@ -59,7 +60,8 @@ typedef enum {
   FATTN_ERR_LAUNCH = -10,     /* the HIP runtime rejected a kernel launch */
   FATTN_ERR_ALIAS = -11,      /* an output pointer equals an input pointer */
   FATTN_ERR_CAUSAL = -12,     /* causal not 0 or 1 */
-  FATTN_ERR_DROPOUT = -13     /* dropout probability not in [0, 1) */
+  FATTN_ERR_DROPOUT = -13,    /* dropout probability not in [0, 1) */
+  FATTN_ERR_SCRATCH = -14     /* problem too large for fattn_bwd_noalloc's static buffer */
 } fattn_status;
 
 /*
@@ -132,6 +134,25 @@ int fattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
               const float* lse, void* dq, void* dk, void* dv,
               int B, int H, int N, int d, float scale, int causal, int dtype,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fattn_bwd without a workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving or training loops, harnesses that forbid allocation). The D
+ * vector lives in a static device buffer of fattn_bwd_noalloc_max_bytes() bytes (16 MiB: D of
+ * up to B * H * N = 4,194,304 rows) that every GPU the library runs on holds until the process
+ * ends; larger problems return FATTN_ERR_SCRATCH before any HIP call. The call performs no
+ * hipMalloc or hipFree. The buffer's device address on a GPU is looked up once, on the first
+ * call there (the GPU of `stream`, or the current one for a NULL stream). Results are bit for bit
+ * those of fattn_bwd. All calls on one GPU share its buffer: calls whose executions overlap on one
+ * GPU (on different streams, or from different threads) race and give undefined results; calls
+ * ordered on one stream are safe. Otherwise the same arguments, checks and results as fattn_bwd.
+ */
+int fattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                      const float* lse, void* dq, void* dk, void* dv,
+                      int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/* Size in bytes of fattn_bwd_noalloc's static buffer (the largest D it can hold). */
+size_t fattn_bwd_noalloc_max_bytes(void);
 
 /*
  * Backward of fattn_fwd_dropout (same p_drop and seed, hence the same mask M): with

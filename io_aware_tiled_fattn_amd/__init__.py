@@ -9,8 +9,8 @@ Low-level names mirror the C entry points (``fattn_fwd``, ``fattn_fwd_tiled``, `
 ``fattn_fwd_splitkv``, ``fattn_fwd_splitkv_workspace_size``,
 ``fattn_splitkv_num_splits``, ``fattn_fwd_partial``, ``fattn_combine``, ``fattn_fwd_kouter``,
 ``fattn_fwd_kouter_workspace_size``, ``fattn_fwd_dropout``, ``fattn_bwd_dropout``,
-``fattn_fwd_blocksparse``, ``fattn_bwd_blocksparse``,
-``fattn_strerror``, ``fattn_version``) and take raw device addresses. ``forward``, ``backward``,
+``fattn_fwd_blocksparse``, ``fattn_bwd_blocksparse``, ``fattn_bwd_noalloc``,
+``fattn_bwd_noalloc_max_bytes``, ``fattn_strerror``, ``fattn_version``) and take raw device addresses. ``forward``, ``backward``,
 ``backward_stages``, ``forward_splitkv``, ``forward_partial``, ``combine`` and ``forward_kouter`` wrap them for
 contiguous torch tensors.
 """
@@ -29,7 +29,7 @@ __all__ = [
     "fattn_fwd_partial", "fattn_combine", "forward_splitkv", "forward_partial", "combine",
     "fattn_fwd_kouter", "fattn_fwd_kouter_workspace_size", "forward_kouter",
     "fattn_fwd_dropout", "fattn_bwd_dropout", "fattn_fwd_blocksparse", "forward_blocksparse",
-    "fattn_bwd_blocksparse", "backward_blocksparse",
+    "fattn_bwd_blocksparse", "backward_blocksparse", "fattn_bwd_noalloc", "fattn_bwd_noalloc_max_bytes",
 ]
 
 FATTN_F32, FATTN_F16, FATTN_BF16 = 0, 1, 2
@@ -96,6 +96,10 @@ def lib():
     L.fattn_fwd_blocksparse.restype = i
     L.fattn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, vp, sz, vp]
     L.fattn_bwd_blocksparse.restype = i
+    L.fattn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    L.fattn_bwd_noalloc.restype = i
+    L.fattn_bwd_noalloc_max_bytes.argtypes = []
+    L.fattn_bwd_noalloc_max_bytes.restype = sz
     L.fattn_strerror.argtypes = [i]
     L.fattn_strerror.restype = ctypes.c_char_p
     L.fattn_version.argtypes = []
@@ -189,6 +193,14 @@ def fattn_bwd_blocksparse(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, ca
                           workspace, workspace_bytes, stream=None) -> int:
     return lib().fattn_bwd_blocksparse(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype,
                                        block_mask, workspace, workspace_bytes, stream)
+
+
+def fattn_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, stream=None) -> int:
+    return lib().fattn_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, stream)
+
+
+def fattn_bwd_noalloc_max_bytes() -> int:
+    return lib().fattn_bwd_noalloc_max_bytes()
 
 
 def fattn_strerror(status: int) -> str:

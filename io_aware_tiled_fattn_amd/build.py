@@ -20,7 +20,8 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libfattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["fattn_api.cpp", "fattn_fwd.hip", "fattn_bwd.hip", "fattn_splitkv.hip", "fattn_kouter.hip"]
+SOURCES = ["fattn_api.cpp", "fattn_fwd.hip", "fattn_bwd.hip", "fattn_splitkv.hip", "fattn_kouter.hip",
+           "fattn_noalloc.hip"]
 
 ARCH = "gfx950"
 COMMON = [

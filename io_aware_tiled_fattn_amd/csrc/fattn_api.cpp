@@ -102,6 +102,7 @@ const char* fattn_strerror(int status) {
     case FATTN_ERR_ALIAS: return "an output aliases an input";
     case FATTN_ERR_CAUSAL: return "causal must be 0 or 1";
     case FATTN_ERR_DROPOUT: return "dropout probability not in [0, 1)";
+    case FATTN_ERR_SCRATCH: return "problem larger than the library's static scratch buffer";
     default: return "unknown status";
   }
 }
@@ -188,11 +189,11 @@ size_t fattn_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
   return fattn::bwd_workspace_bytes(B, H, N, d);
 }
 
-// Argument checks shared by the full backward entry points (extra: one more input, may be null).
-static int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                     const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
-                     float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
-                     const void* extra) {
+// Argument checks shared by the full backward entry points (extra: one more input, may be null),
+// except for the workspace.
+static int check_bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                          const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                          float scale, int causal, int dtype, const void* extra) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FATTN_ERR_NULL;
   int st = check_common(B, H, N, d, dtype);
   if (st != FATTN_OK) return st;
@@ -209,13 +210,22 @@ static int check_bwd(const void* q, const void* k, const void* v, const void* o,
     for (const void* s2 : ins)
       if (s2 && p == s2) return FATTN_ERR_ALIAS;
   if (dq == dk || dq == dv || dk == dv) return FATTN_ERR_ALIAS;
+  return FATTN_OK;
+}
+
+// ... and with the caller's workspace.
+static int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                     float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                     const void* extra) {
+  int st = check_bwd_args(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, extra);
+  if (st != FATTN_OK) return st;
   const size_t need = fattn::bwd_workspace_bytes(B, H, N, d);
   if (!workspace || workspace_bytes < need) return FATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FATTN_ERR_ALIGN;
-  for (void* p : outs)
-    if (p == workspace) return FATTN_ERR_ALIAS;
-  for (const void* s2 : ins)
-    if (s2 == workspace) return FATTN_ERR_ALIAS;
+  const void* all[10] = {dq, dk, dv, q, k, v, o, dO, lse, extra};
+  for (const void* p : all)
+    if (p && p == workspace) return FATTN_ERR_ALIAS;
   return FATTN_OK;
 }
 
@@ -241,6 +251,24 @@ int fattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
                      workspace_bytes, nullptr);
   if (st != FATTN_OK) return st;
   fattn::BwdReq r{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, (float*)workspace};
+  return launch_status(fattn::launch_bwd(r, (hipStream_t)stream));
+}
+
+size_t fattn_bwd_noalloc_max_bytes(void) { return fattn::scratch_capacity(); }
+
+int fattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                      const float* lse, void* dq, void* dk, void* dv,
+                      int B, int H, int N, int d, float scale, int causal, int dtype, void* stream) {
+  // fattn_bwd's checks, then the size of the static buffer, all before any HIP call
+  int st = check_bwd_args(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, nullptr);
+  if (st != FATTN_OK) return st;
+  if (fattn::bwd_workspace_bytes(B, H, N, d) > fattn::scratch_capacity()) return FATTN_ERR_SCRATCH;
+  int device = -1;
+  hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &device) : hipGetDevice(&device);
+  if (e != hipSuccess) return FATTN_ERR_LAUNCH;
+  void* ws = nullptr;
+  if (fattn::scratch_address(device, &ws) != hipSuccess) return FATTN_ERR_LAUNCH;
+  fattn::BwdReq r{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, (float*)ws};
   return launch_status(fattn::launch_bwd(r, (hipStream_t)stream));
 }
 

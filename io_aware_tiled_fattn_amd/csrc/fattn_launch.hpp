@@ -51,6 +51,11 @@ bool fwd_tile_supported(int dtype, int d, int Br, int Bc);
 hipError_t launch_fwd(const FwdReq& r, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
+
+// The static device buffer of the no-allocation backward (fattn_noalloc.hip): its size, and the
+// device address of `device`'s copy (resolved once per device, with that device current).
+size_t scratch_capacity();
+hipError_t scratch_address(int device, void** out);
 // stage: 0 = preprocess, 1 = dK/dV, 2 = dQ; -1 = preprocess, dK/dV, dQ in order
 hipError_t launch_bwd(const BwdReq& r, hipStream_t stream, int stage = -1);
 

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(L):
             "fattn_fwd_splitkv_workspace_size", "fattn_splitkv_num_splits", "fattn_fwd_partial",
             "fattn_combine", "fattn_fwd_kouter", "fattn_fwd_kouter_workspace_size",
             "fattn_fwd_dropout", "fattn_bwd_dropout", "fattn_fwd_blocksparse",
-            "fattn_bwd_blocksparse"} <= set(names)
+            "fattn_bwd_blocksparse", "fattn_bwd_noalloc", "fattn_bwd_noalloc_max_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
         assert getattr(fa, n) is not None
@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_strerror(L):
     assert fa.fattn_version() >= 100
-    for code in range(0, -14, -1):
+    for code in range(0, -15, -1):
         s = fa.fattn_strerror(code)
         assert s and s != "unknown status", code
     assert fa.fattn_strerror(12345) == "unknown status"
@@ -288,3 +288,28 @@ def test_bwd_blocksparse_rejects_bad_arguments(L, kw, status):
     m = a["m"]
     assert fa.fattn_bwd_blocksparse(P[0], P[1], P[2], P[3], P[4], P[5], a["dq"], a["dk"], P[8], 1, 2, a["N"],
                                     a["d"], a["scale"], a["causal"], a["dtype"], m, a["ws"], a["wsb"]) == status
+
+
+def bwd_noalloc(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], dO=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[8],
+             B=2, H=3, N=100, d=128, scale=0.088, causal=1, dtype=fa.FATTN_BF16, stream=None)
+    a.update(kw)
+    return fa.fattn_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["dO"], a["lse"], a["dq"], a["dk"],
+                                a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                                a["dtype"], a["stream"])
+
+
+def test_bwd_noalloc_buffer_size(L):
+    assert fa.fattn_bwd_noalloc_max_bytes() == 16 << 20
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(dv=0), -1), (dict(d=96), -3), (dict(dtype=fa.FATTN_F32), -4),
+    (dict(N=0), -2), (dict(causal=2), -12), (dict(scale=math.inf), -7), (dict(dk=MIS), -6),
+    (dict(dq=P[0]), -11), (dict(dk=P[6]), -11),
+    # the D vector of B * H * N rows must fit the 16 MiB static buffer (4,194,304 rows)
+    (dict(B=1, H=1, N=4194305), -14), (dict(B=4, H=8, N=131073), -14),
+    (dict(B=64, H=64, N=1025, d=64), -14),
+])
+def test_bwd_noalloc_rejects_bad_arguments(L, kw, status):
+    assert bwd_noalloc(**kw) == status
