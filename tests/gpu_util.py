@@ -64,7 +64,7 @@ def every_head(B, H):
     return [(b, h) for b in range(B) for h in range(H)]
 
 
-_SENTINEL = {2: 0x7E5A, 4: 0x7FC0DEAD}  # bit patterns no kernel output here can take
+_SENTINEL = {1: 0x5A, 2: 0x7E5A, 4: 0x7FC0DEAD}  # bit patterns no kernel output here can take
 
 
 class Guarded:
@@ -80,9 +80,9 @@ class Guarded:
         n = math.prod(self.shape)
         self.buf = torch.empty(n + 2 * guard, dtype=dtype, device=device)
         size = self.buf.element_size()
-        self.ints = self.buf.view(torch.int16 if size == 2 else torch.int32)
+        self.ints = self.buf.view({1: torch.int8, 2: torch.int16, 4: torch.int32}[size])
         pat = _SENTINEL[size]
-        self.pat = pat - (1 << 16) if size == 2 and pat >= 1 << 15 else pat
+        self.pat = pat - (1 << (8 * size)) if pat >= 1 << (8 * size - 1) else pat
         self.ints.fill_(self.pat)
         self.t = self.buf[guard: guard + n].view(self.shape)
 
