@@ -302,13 +302,19 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  // query tile i's mask block: row (i BQ) / 128, column jt (BKV = 128)
-  const uint8_t* bcol = SPARSE ? a.bmask + (size_t)bh * a.nb * a.nb + jt : nullptr;
+  // query tile i's mask block: row (i BQ) / 128, column jt (BKV = 128); the column's allowed rows
+  // are scanned 64 at a time (MaskLine)
+  static_assert(BKV == 128 && 128 % BQ == 0, "a dK/dV work-group is one mask column");
+  constexpr int TPR = 128 / BQ;  // query tiles per mask row
+  MaskLine mcol = mask_line(SPARSE ? a.bmask + (size_t)bh * a.nb * a.nb + jt : nullptr, a.nb, SPARSE ? a.nb : 0);
+  // the visited tile after i: the next tile of i's mask row, else the first of the next allowed row
   auto next = [&](int i) {
-    ++i;
-    if (SPARSE)
-      while (i < n_qt && bcol[(size_t)((i * BQ) >> 7) * a.nb] == 0) ++i;
-    return i;
+    const int ii = i + 1;
+    if (!SPARSE) return ii;
+    if (ii >= n_qt) return n_qt;
+    if (ii % TPR != 0) return ii;
+    const int r = mask_next(mcol, ii / TPR, lane);
+    return r >= (n_qt + TPR - 1) / TPR ? n_qt : r * TPR;
   };
   // A dense run visits the tiles i_begin, i_begin + 1, ...; a block-sparse run only the allowed
   // ones. Either way the visited tiles take positions 0, 1, ...
@@ -619,22 +625,31 @@ __global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  // mask rows of this work-group and of this wave; key tile j lies in mask column (j BK) / 128
+  // The work-group's 256 queries are two mask rows (waves 0-3 the first, 4-7 the second); key
+  // tile j lies in mask column j / TPC. The work-group visits the tiles whose column is set in
+  // either row, each wave computes those its own row allows; both rows are scanned 64 columns at
+  // a time (MaskLine), only right after the vmcnt wait that empties the prefetch queue.
+  static_assert(BQ == 256 && 128 % BK == 0, "a dQ work-group is two mask rows");
+  constexpr int TPC = 128 / BK;  // key tiles per mask column
+  const int r_lo = q_base >> 7;
   const uint8_t* bm = SPARSE ? a.bmask + (size_t)bh * a.nb * a.nb : nullptr;
-  const int r_lo = q_base >> 7, r_hi = min(a.nb, (q_base + BQ + 127) >> 7);
-  const int wave_row = min(q0, N - 1) >> 7;
+  MaskLine row0 = mask_line(SPARSE ? bm + (size_t)r_lo * a.nb : nullptr, 1, SPARSE ? a.nb : 0);
+  MaskLine row1 = mask_line(SPARSE && r_lo + 1 < a.nb ? bm + (size_t)(r_lo + 1) * a.nb : nullptr, 1,
+                            SPARSE && r_lo + 1 < a.nb ? a.nb : 0);
+  const bool second_row = w >= 4;
+  bool wave_on = true, wave_on_next = true;  // this wave's row allows the current / next tile
   auto next = [&](int j) {
-    ++j;
-    if (SPARSE)
-      while (j < n_kv) {
-        bool on = false;
-        for (int r = r_lo; r < r_hi; ++r) on = on || bm[(size_t)r * a.nb + ((j * BK) >> 7)] != 0;
-        if (on) break;
-        ++j;
-      }
-    return j;
+    const int jj = j + 1;
+    if (!SPARSE) return jj;
+    if (jj >= n_kv) return n_kv;
+    if (jj % TPC != 0) return jj;  // the same column: the wave's flag carries over
+    const int c0 = mask_next(row0, jj / TPC, lane), c1 = mask_next(row1, jj / TPC, lane);
+    const int c = min(c0, c1);
+    wave_on_next = (second_row ? c1 : c0) == c;
+    return c >= (n_kv + TPC - 1) / TPC ? n_kv : c * TPC;
   };
   int j = next(-1);
+  wave_on = wave_on_next;
   if (j < n_kv) issue(j, 0);
   for (int t = 0; j < n_kv; ++t) {
     wait_vmcnt<0>();
@@ -642,10 +657,11 @@ __global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)
     const int jn = next(j);
     if (jn < n_kv) issue(jn, t + 1);
     const int k0 = j * BK;
-    const int jc = j;
+    const bool on = wave_on;
+    wave_on = wave_on_next;
     j = jn;
     if (!(wave_active && k0 < wave_kv_end)) continue;
-    if (SPARSE && bm[(size_t)wave_row * a.nb + ((jc * BK) >> 7)] == 0) continue;
+    if (SPARSE && !on) continue;
     const uint8_t* Ks = smem + (t & 1) * Cfg::STAGE_B;
     const uint8_t* Vs = Ks + TILE_B;
     const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > q0);

@@ -184,6 +184,40 @@ __device__ inline uint32_t quad_keep_bits(uint32_t kgroup, uint32_t q4, uint32_t
          (((quad_bcast<2>(m) >> r) & 1u) << 2) | (((quad_bcast<3>(m) >> r) & 1u) << 3);
 }
 
+// ---- block-mask scans ------------------------------------------------------------------------
+// One line of a block mask (a mask row, or a mask column read with a stride), 64 entries at a
+// time: lane l tests entry base + l, and a ballot turns the 64 tests into one wave-uniform bit
+// set, so the next allowed entry is found by a scalar bit scan instead of one dependent memory
+// load per entry. Windows are loaded only where no tile prefetch is in flight (right after a
+// tile loop's vmcnt wait), so the load waits for nothing but itself.
+struct MaskLine {
+  const uint8_t* p;  // entry e at p[e * stride]
+  long long stride;
+  int n;             // entries in the line (0: an empty line)
+  int base;          // first entry of the loaded window (negative before the first load)
+  uint64_t bits;     // bit i: entry base + i is nonzero
+};
+__device__ inline MaskLine mask_line(const uint8_t* p, long long stride, int n) {
+  return MaskLine{p, stride, n, -64, 0ull};
+}
+// Smallest allowed entry >= e, or 0x7fffffff if there is none.
+__device__ inline int mask_next(MaskLine& m, int e, int lane) {
+  if (e < 0) e = 0;
+  while (e < m.n) {
+    if (e < m.base || e >= m.base + 64) {
+      const int base = e & ~63;
+      const int x = base + lane;
+      const bool on = x < m.n && m.p[(size_t)x * m.stride] != 0;
+      m.bits = __builtin_amdgcn_ballot_w64(on);
+      m.base = base;
+    }
+    const uint64_t rest = m.bits >> (e - m.base);
+    if (rest) return e + (int)__builtin_ctzll(rest);
+    e = m.base + 64;
+  }
+  return 0x7fffffff;
+}
+
 // Causal grid order within one XCD: its hpx heads are taken `group` at a time, and inside a group
 // the tiles of all its heads run longest first (rank 0 = longest), so the triangular work stays
 // balanced while at most `group` heads' K/V (or Q/dO) compete for the XCD's L2. `local` runs over

@@ -253,12 +253,20 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
         for (int e = 0; e < 16; ++e)
           s[kb][e] = (kb * 32 + 8 * (e >> 2) + (e & 3) > lim) ? -__builtin_inff() : s[kb][e];
     }
-    float mx = -__builtin_inff();
+    // one max chain per 32-key block, then across them: BC / 32 short dependent chains instead of
+    // one of BC / 2 steps (both waves of a SIMD reach this point together, so its latency shows)
+    float mk[BC / 32];
 #pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb)
+    for (int kb = 0; kb < BC / 32; ++kb) {
+      mk[kb] = -__builtin_inff();
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    return max_halves(mx) * a.c;  // c > 0, so this is the max of the log2-domain logits
+      for (int e = 0; e < 16; ++e) mk[kb] = fmaxf(mk[kb], s[kb][e]);
+    }
+#pragma unroll
+    for (int w2 = BC / 64; w2 >= 1; w2 >>= 1)
+#pragma unroll
+      for (int kb = 0; kb < w2; ++kb) mk[kb] = fmaxf(mk[kb], mk[kb + w2]);
+    return max_halves(mk[0]) * a.c;  // c > 0, so this is the max of the log2-domain logits
   };
   // P^T = exp2(s*c - m_ref) (masked scores are -inf and give 0), packed to 16-bit MFMA B
   // fragments (8 keys per 16-key chunk), then O^T += V^T P^T with V^T fragments from the
@@ -361,23 +369,20 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
       ++j;
     }
   } else {
-    // Block-sparse: the work-group visits the key tiles whose mask column is set for any of its
-    // mask rows, in order, two stages deep (stage = position in that sequence); each wave
-    // computes the ones its own mask row allows.
+    // Block-sparse: the work-group's 128 query rows are one mask row; it visits the key tiles
+    // whose mask column is set in that row, in order, two stages deep (stage = position in that
+    // sequence). The row's allowed columns are scanned 64 at a time (MaskLine).
     static_assert(NS == 2, "block-sparse runs use two stages");
-    const uint8_t* bm = a.bmask + (size_t)bh * a.nb * a.nb;
-    const int r_lo = q_base / 128, r_hi = min(a.nb, (q_base + BR + 127) / 128);
-    const int wave_row = min(q0, N - 1) / 128;
-    auto col = [&](int j) { return (j * BC) / 128; };
-    auto wg_on = [&](int j) {
-      bool on = false;
-      for (int r = r_lo; r < r_hi; ++r) on = on || bm[(size_t)r * a.nb + col(j)] != 0;
-      return on;
-    };
+    static_assert(BR == 128 && 128 % BC == 0, "a block-sparse work-group is one mask row");
+    constexpr int TPC = 128 / BC;  // key tiles per mask column
+    MaskLine row = mask_line(a.bmask + ((size_t)bh * a.nb + qt) * a.nb, 1, a.nb);
+    // the visited tile after j: the next tile of j's column, else the first of the next allowed one
     auto next = [&](int j) {
-      ++j;
-      while (j < n_kv && !wg_on(j)) ++j;
-      return j;
+      const int jj = j + 1;
+      if (jj >= n_kv) return n_kv;
+      if (jj % TPC != 0) return jj;
+      const int c = mask_next(row, jj / TPC, lane);
+      return c >= (n_kv + TPC - 1) / TPC ? n_kv : c * TPC;
     };
     int j = next(-1), t = 0;
     if (j < n_kv) issue(j, 0);
@@ -389,7 +394,7 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
         barrier_lds();
         jn = next(j);
         if (jn < n_kv) issue(jn, t + 1);
-        if (!(wave_active && j * BC < wave_kv_end && bm[(size_t)wave_row * a.nb + col(j)] != 0)) continue;
+        if (!(wave_active && j * BC < wave_kv_end)) continue;
         const float mx = scores(j, t, s);
         m_new = fmaxf(m_ref, mx);
         if (wave_any(m_new > m_ref + kRescaleSlack)) {
