@@ -161,6 +161,48 @@ def n_sweep(torch, fa):
     return 0
 
 
+def kernel_pass(torch, fa, fi, reps=3):
+    """Each kernel of the step a few times, for counter passes (rocprofv3 --pmc ...): the causal
+    forward on the prefill (B=4) and step (B=2) workloads, the backward's stage entry points and
+    fattn_bwd on the step workload, the long-context forward (B=1 H=32 N=16384) with both masks,
+    then a 256 MiB + 256 MiB calibration copy. Inputs are the seeded workloads' own."""
+    w5 = fi.WORKLOADS[5]
+    B, H, N, d = w5.shape
+    q, k, v, do = _upload(fi.workload_inputs(5), torch)
+    o, lse = fa.forward(q, k, v, causal=True)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dvec = torch.empty(B * H * N, dtype=torch.float32, device="cuda")
+    q3, k3, v3, _ = _upload(fi.workload_inputs(3), torch)
+    o3, l3 = fa.forward(q3, k3, v3, causal=True)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + 0.5  # steady clocks before the counted launches
+    while time.perf_counter() < t_end:
+        fa.forward(q3, k3, v3, causal=True, out=o3, lse=l3)
+        fa.backward(q, k, v, o, do, lse, causal=True)
+        torch.cuda.synchronize()
+    for _ in range(reps):
+        fa.forward(q3, k3, v3, causal=True, out=o3, lse=l3)
+        fa.forward(q, k, v, causal=True, out=o, lse=lse)
+        fa.backward_stages(q, k, v, o, do, lse, dq, dk, dv, dvec, causal=True)
+        fa.backward(q, k, v, o, do, lse, causal=True, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    del q3, k3, v3, o3, l3
+    q4, k4, v4, _ = _upload(fi.workload_inputs(4), torch)
+    o4, l4 = fa.forward(q4, k4, v4, causal=True)
+    for causal in (True, False):
+        for _ in range(reps):
+            fa.forward(q4, k4, v4, causal=causal, out=o4, lse=l4)
+    torch.cuda.synchronize()
+    del q4, k4, v4, o4, l4
+    src = torch.ones(128 * 2**20, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel_pass": "done", "reps": reps}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +220,9 @@ def main(argv=None):
                     help="only run the forward and the backward at N = 1024 .. 16384 (B=1, H=16, d=128, bf16, causal and "
                          "non-causal) a few times each, plus the calibration copy, for the HBM-bytes-vs-N "
                          "counters; prints one JSON line with the per-N times")
+    ap.add_argument("--kernel-pass", action="store_true",
+                    help="only run each step kernel (and the long-context forward, and a calibration "
+                         "copy) a few times, for rocprofv3 counter passes; prints one JSON line")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the kernels shard over (batch, head) with no "
@@ -192,6 +237,8 @@ def main(argv=None):
     fa.lib()
     if a.n_sweep:
         return n_sweep(torch, fa)
+    if a.kernel_pass:
+        return kernel_pass(torch, fa, fi)
     w5, w3 = fi.WORKLOADS[5], fi.WORKLOADS[3]
     B, H, N, d = w5.shape
 

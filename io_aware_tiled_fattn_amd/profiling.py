@@ -41,6 +41,24 @@ COMMANDS = {
 }
 
 
+# Where the cycles of the step kernels go: two SQ counter passes over bench.py's kernel pass
+# (each pass at most 8 SQ counters, plus GRBM_GUI_ACTIVE for the engine clock).
+STALL_COUNTERS = {
+    "sq1": "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
+           "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE",
+    "sq2": "SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_INSTS_VALU SQ_INSTS_MFMA "
+           "SQ_INSTS_LDS SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_SALU GRBM_GUI_ACTIVE",
+}
+STALL_COMMANDS = {
+    key: "rocprofv3 --pmc " + ctrs + " --output-format csv -d {run}/" + key + " -o run -- "
+         "python -u bench.py --kernel-pass"
+    for key, ctrs in STALL_COUNTERS.items()
+}
+# Algorithmic FLOPs per launch of the step kernels at B=2 H=16 N=4096 d=128 causal (B=4 for the
+# prefill forward), per the stated convention (each GEMM 2 N^2 d per head, halved for causal).
+_F5 = 4.0 * 2 * 16 * 4096 * 4096 * 128 / 2
+
+
 # HBM bytes versus N for the forward and the backward (evidence that traffic stays O(N d)).
 SWEEP_COMMANDS = {
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {run}/fetch -o run -- "
@@ -149,6 +167,124 @@ def mfma_busy(run_dir):
     return {key: sum(v) / len(v) for key, v in per.items()}
 
 
+def kernel_stats_by_grid(run_dir):
+    """Per-(kernel, grid) launch counts and durations from the kernel trace."""
+    path = _find(run_dir, "trace", "kernel_trace.csv")
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        grid = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y") or 1) * int(r.get("Grid_Size_Z") or 1)
+        per[(short_name(r["Kernel_Name"]), grid)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    total = sum(sum(v) for v in per.values()) or 1
+    out = []
+    for (name, grid), v in sorted(per.items()):
+        out.append({"kernel": name, "grid": grid, "calls": len(v), "avg_us": sum(v) / len(v) / 1e3,
+                    "min_us": min(v) / 1e3, "max_us": max(v) / 1e3, "pct": 100.0 * sum(v) / total})
+    return out
+
+
+def _per_dispatch(path):
+    """{dispatch: {"kernel", "grid", "ns", counter: value}} from one counter-collection CSV."""
+    out = {}
+    for r in csv.DictReader(open(path)):
+        d = out.setdefault(int(r["Dispatch_Id"]), {"kernel": short_name(r["Kernel_Name"]),
+                                                  "grid": int(r["Grid_Size"]),
+                                                  "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+# the step kernels whose counters the stall summary reports: (label, signature, grid, FLOPs)
+STALL_KERNELS = (
+    ("forward, prefill B=4", "fwd_kernel<Bf16, 128, 256, 128, 2, true, false, false, false>", 1048576 // 2, 2 * _F5),
+    ("forward, step B=2", "fwd_kernel<Bf16, 128, 256, 128, 2, true, false, false, false>", 262144, _F5),
+    ("dK/dV (wave pairs)", "bwd_dkdv_pair_kernel<Bf16, 128, true, false, false, false>", 524288, 2 * _F5),
+    ("dQ, computing D (in fattn_bwd)", "bwd_dq_kernel<Bf16, 128, true, false, false, false, true>", 262144, 1.5 * _F5),
+    ("dQ, D given (stage entry point)", "bwd_dq_kernel<Bf16, 128, true, false, false, false, false>", 262144, 1.5 * _F5),
+)
+
+
+def stall_table(run_dir, peak_tflops=2516.6, max_mhz=2400.0):
+    """Per step kernel: time, engine clock, MFMA busy, and where the waves' cycles go, from the
+    two SQ counter passes (STALL_COMMANDS)."""
+    d1 = _per_dispatch(_find(run_dir, "sq1", "counter_collection.csv"))
+    d2 = _per_dispatch(_find(run_dir, "sq2", "counter_collection.csv"))
+    rows = []
+    for label, sig, grid, flops in STALL_KERNELS:
+        a = [v for v in d1.values() if v["kernel"].startswith(sig) and v["grid"] == grid]
+        b = [v for v in d2.values() if v["kernel"].startswith(sig) and v["grid"] == grid]
+        if not a or not b:
+            continue
+        mean = lambda xs, k: sum(x[k] for x in xs) / len(xs)
+        ns = (mean(a, "ns") + mean(b, "ns")) / 2
+        cyc = mean(b, "GRBM_GUI_ACTIVE") / 8.0  # GRBM_GUI_ACTIVE is summed over the 8 XCDs
+        mhz = cyc / (ns * 1e-3)
+        wave = mean(a, "SQ_WAVE_CYCLES")
+        mfma = mean(b, "SQ_INSTS_MFMA")
+        row = {"label": label, "kernel": sig, "grid": grid, "calls": len(a) + len(b), "us": ns / 1e3,
+               "mhz": mhz,
+               "mfma_busy": mean(b, "SQ_VALU_MFMA_BUSY_CYCLES") / (1024.0 * cyc),
+               "coexec": mean(b, "SQ_VALU_MFMA_COEXEC_CYCLES") / (1024.0 * cyc),
+               "issuing": mean(a, "SQ_ACTIVE_INST_ANY") / wave,
+               "wait_any": mean(a, "SQ_WAIT_ANY") / wave,
+               "wait_issue": mean(a, "SQ_WAIT_INST_ANY") / wave,
+               "valu_active": mean(a, "SQ_ACTIVE_INST_VALU") / wave,
+               "lds_active": mean(a, "SQ_ACTIVE_INST_LDS") / wave,
+               "lds_wait": mean(a, "SQ_WAIT_INST_LDS") / wave,
+               "bank_conflict": mean(b, "SQ_LDS_BANK_CONFLICT"),
+               "valu_per_mfma": (mean(b, "SQ_INSTS_VALU") - mfma) / mfma if mfma else None,
+               "lds_per_mfma": mean(b, "SQ_INSTS_LDS") / mfma if mfma else None,
+               "salu_per_mfma": mean(b, "SQ_INSTS_SALU") / mfma if mfma else None}
+        if flops:
+            tf = flops / (ns * 1e-9) / 1e12
+            row["tflops"] = tf
+            row["frac_nominal"] = tf / peak_tflops
+            row["frac_clock"] = tf / (peak_tflops * mhz / max_mhz)
+        rows.append(row)
+    return rows
+
+
+def write_stalls(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
+    os.makedirs(prof_dir, exist_ok=True)
+    rows = stall_table(run_dir)
+    pct = lambda x: "—" if x is None else f"{x:.1%}"
+    num = lambda x, f="{:.2f}": "—" if x is None else f.format(x)
+    lines = [f"# Where the step kernels' cycles go — {workload} (and the B=4 prefill forward)\n",
+             "Commands (from the repository root, on the GPU box; RUN is an output folder):\n"]
+    for key in ("sq1", "sq2"):
+        lines.append("    " + STALL_COMMANDS[key].format(run="RUN"))
+    lines += ["",
+              "Every figure is the mean over the kernel's launches in the pass (bench.py --kernel-pass "
+              "runs each three times after 0.5 s of warm-up).",
+              "- Engine clock = GRBM_GUI_ACTIVE / 8 XCDs / kernel duration (the counter runs at the "
+              "engine clock and is summed over the XCDs). The nominal peak (2516.6 TFLOP/s) assumes "
+              "2400 MHz; the clock-adjusted fraction divides by the peak at the measured clock.",
+              "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles); co-issue = "
+              "SQ_VALU_MFMA_COEXEC_CYCLES (a VALU instruction issued while the MFMA unit was busy) on "
+              "the same base.",
+              "- Wave-time shares (each over SQ_WAVE_CYCLES, all in quad-cycles summed over waves): "
+              "issuing = SQ_ACTIVE_INST_ANY, waiting = SQ_WAIT_ANY (for a dependency, a count or a "
+              "barrier), waiting for an issue slot = SQ_WAIT_INST_ANY, VALU = SQ_ACTIVE_INST_VALU, "
+              "LDS = SQ_ACTIVE_INST_LDS, LDS issue wait = SQ_WAIT_INST_LDS. Two waves share each "
+              "SIMD, so a wave waits for an issue slot whenever the other one issues.",
+              "- Instruction mix per MFMA from SQ_INSTS_VALU (less the MFMAs), SQ_INSTS_LDS and "
+              "SQ_INSTS_SALU.", "",
+              "| kernel | us | clock MHz | TFLOP/s | of nominal peak | of clock-adjusted peak | MFMA busy | co-issue | bank-conflict cycles |",
+              "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['label']} (`{r['kernel']}`) | {r['us']:.1f} | {r['mhz']:.0f} | "
+                     f"{num(r.get('tflops'), '{:.0f}')} | {pct(r.get('frac_nominal'))} | {pct(r.get('frac_clock'))} | "
+                     f"{pct(r['mfma_busy'])} | {pct(r['coexec'])} | {r['bank_conflict']:.0f} |")
+    lines += ["", "| kernel | issuing | waiting | waiting for an issue slot | VALU | LDS | LDS issue wait | VALU / MFMA | LDS / MFMA | SALU / MFMA |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['label']} | {pct(r['issuing'])} | {pct(r['wait_any'])} | {pct(r['wait_issue'])} | "
+                     f"{pct(r['valu_active'])} | {pct(r['lds_active'])} | {pct(r['lds_wait'])} | "
+                     f"{num(r['valu_per_mfma'])} | {num(r['lds_per_mfma'])} | {num(r['salu_per_mfma'])} |")
+    with open(os.path.join(prof_dir, f"stalls_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return rows
+
+
 def _is_decode(kernel):
     return any(kernel.startswith(d) for d in DECODE_KERNELS)
 
@@ -188,7 +324,7 @@ def _live_vs_trace(run_dir, stats):
 
 def write_summaries(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
     os.makedirs(prof_dir, exist_ok=True)
-    stats = kernel_stats(run_dir)
+    stats = kernel_stats_by_grid(run_dir)
     tr, fc, wc = traffic(run_dir)
     busy = mfma_busy(run_dir)
     for t in tr:
@@ -211,10 +347,11 @@ def write_summaries(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
         pick = (lambda k: _is_decode(k)) if wl == DECODE_WORKLOAD else (lambda k: not _is_decode(k))
         lines = [f"# Kernel times — {title}\n",
                  cmd_note + "    " + COMMANDS["trace"].format(run="RUN") + "\n",
-                 "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+                 "One row per (kernel, grid): the grid (threads) tells the workloads apart.\n",
+                 "| kernel | grid | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|---|"]
         for s in stats:
             if pick(s["kernel"]):
-                lines.append(f"| `{s['kernel']}` | {s['calls']} | {s['avg_us']:.1f} | {s['min_us']:.1f} | "
+                lines.append(f"| `{s['kernel']}` | {s['grid']} | {s['calls']} | {s['avg_us']:.1f} | {s['min_us']:.1f} | "
                              f"{s['max_us']:.1f} | {s['pct']:.1f} |")
         lines.append("\n" + note + " % time is over every kernel of the run.")
         if wl != DECODE_WORKLOAD:
@@ -348,6 +485,10 @@ if __name__ == "__main__":
             with open(sys.argv[4]) as f:
                 times = json.loads(f.read().strip().splitlines()[-1])["runs"]
         for r in write_sweep(sys.argv[2], sys.argv[3], times):
+            print(r)
+        sys.exit(0)
+    if sys.argv[1] == "stalls":
+        for r in write_stalls(sys.argv[2], sys.argv[3]):
             print(r)
         sys.exit(0)
     run = sys.argv[1]

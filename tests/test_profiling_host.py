@@ -71,3 +71,65 @@ def test_roofline_traffic_fields():
     assert out["mfma_busy"] == 0.4234
     assert "mfma_busy" not in bench.traffic_fields({"fetch_bytes": 1.0, "write_bytes": 2.0})
 
+
+
+DKDV = ("fattn::(anonymous namespace)::bwd_dkdv_pair_kernel<Bf16, 128, true, false, false, false>"
+        "(fattn::(anonymous namespace)::BwdArgs)")
+
+
+def _write_timed(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    keys = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value", "Start_Timestamp",
+            "End_Timestamp"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=keys)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_stall_table_clock_busy_and_shares(tmp_path):
+    # one dK/dV launch of 100 us at 2000 MHz: 200,000 cycles per XCD, GRBM_GUI_ACTIVE summed over
+    # the 8 XCDs; half of the 1024 SIMDs' cycles with the MFMA unit busy
+    ns = 100_000
+    cyc = 200_000
+    t = lambda did, c, v: {"Dispatch_Id": did, "Kernel_Name": DKDV, "Grid_Size": 524288, "Counter_Name": c,
+                           "Counter_Value": v, "Start_Timestamp": 1000, "End_Timestamp": 1000 + ns}
+    sq1 = [t(1, "SQ_WAVE_CYCLES", 1000.0), t(1, "SQ_ACTIVE_INST_ANY", 350.0), t(1, "SQ_WAIT_ANY", 300.0),
+           t(1, "SQ_WAIT_INST_ANY", 340.0), t(1, "SQ_ACTIVE_INST_VALU", 180.0), t(1, "SQ_ACTIVE_INST_LDS", 70.0),
+           t(1, "SQ_WAIT_INST_LDS", 50.0), t(1, "SQ_BUSY_CYCLES", 1.0), t(1, "GRBM_GUI_ACTIVE", 8.0 * cyc)]
+    sq2 = [t(2, "SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * 1024 * cyc), t(2, "SQ_VALU_MFMA_COEXEC_CYCLES", 0.1 * 1024 * cyc),
+           t(2, "SQ_INSTS_MFMA", 1000.0), t(2, "SQ_INSTS_VALU", 5000.0), t(2, "SQ_INSTS_LDS", 2000.0),
+           t(2, "SQ_INSTS_SALU", 2500.0), t(2, "SQ_LDS_BANK_CONFLICT", 0.0), t(2, "SQ_LDS_IDX_ACTIVE", 1.0),
+           t(2, "GRBM_GUI_ACTIVE", 8.0 * cyc)]
+    _write_timed(str(tmp_path / "sq1" / "run_counter_collection.csv"), sq1)
+    _write_timed(str(tmp_path / "sq2" / "run_counter_collection.csv"), sq2)
+    (r,) = profiling.stall_table(str(tmp_path))
+    assert r["label"].startswith("dK/dV") and r["calls"] == 2
+    assert abs(r["us"] - 100.0) < 1e-9 and abs(r["mhz"] - 2000.0) < 1e-9
+    assert abs(r["mfma_busy"] - 0.5) < 1e-12 and abs(r["coexec"] - 0.1) < 1e-12
+    assert abs(r["issuing"] - 0.35) < 1e-12 and abs(r["wait_any"] - 0.3) < 1e-12
+    assert abs(r["wait_issue"] - 0.34) < 1e-12 and abs(r["lds_wait"] - 0.05) < 1e-12
+    assert abs(r["valu_per_mfma"] - 4.0) < 1e-12 and abs(r["lds_per_mfma"] - 2.0) < 1e-12
+    assert abs(r["salu_per_mfma"] - 2.5) < 1e-12
+    # 4 dK/dV GEMMs at B=2 H=16 N=4096 d=128, causal, in 100 us; the peak scales with the clock
+    flops = 2 * 4.0 * 2 * 16 * 4096 * 4096 * 128 / 2
+    assert abs(r["tflops"] - flops / 1e-4 / 1e12) < 1e-6
+    assert abs(r["frac_clock"] - r["frac_nominal"] * 2400 / 2000) < 1e-12
+    profiling.write_stalls(str(tmp_path), str(tmp_path / "out"))
+    assert os.path.exists(str(tmp_path / "out" / "stalls_b2h16n4096d128_causal_bf16.md"))
+
+
+def test_kernel_times_are_split_by_grid(tmp_path):
+    path = tmp_path / "trace" / "run_kernel_trace.csv"
+    os.makedirs(os.path.dirname(str(path)), exist_ok=True)
+    with open(str(path), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X",
+                                          "Grid_Size_Y", "Grid_Size_Z"])
+        w.writeheader()
+        for grid, dur in ((262144, 100), (262144, 300), (524288, 1000)):
+            w.writerow({"Kernel_Name": KERN, "Start_Timestamp": 0, "End_Timestamp": dur, "Grid_Size_X": grid,
+                        "Grid_Size_Y": 1, "Grid_Size_Z": 1})
+    rows = {r["grid"]: r for r in profiling.kernel_stats_by_grid(str(tmp_path))}
+    assert rows[262144]["calls"] == 2 and abs(rows[262144]["avg_us"] - 0.2) < 1e-12
+    assert rows[524288]["calls"] == 1 and abs(rows[524288]["pct"] - 1000 / 14) < 1e-9
