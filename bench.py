@@ -164,8 +164,9 @@ def n_sweep(torch, fa):
 def kernel_pass(torch, fa, fi, reps=3):
     """Each kernel of the step a few times, for counter passes (rocprofv3 --pmc ...): the causal
     forward on the prefill (B=4) and step (B=2) workloads, the backward's stage entry points and
-    fattn_bwd on the step workload, the long-context forward (B=1 H=32 N=16384) with both masks,
-    then a 256 MiB + 256 MiB calibration copy. Inputs are the seeded workloads' own."""
+    fattn_bwd on the step workload, the dropout and block-sparse forward and backward on the
+    step's shape, the long-context forward (B=1 H=32 N=16384) with both masks, then a
+    256 MiB + 256 MiB calibration copy. Inputs are the seeded workloads' own."""
     w5 = fi.WORKLOADS[5]
     B, H, N, d = w5.shape
     q, k, v, do = _upload(fi.workload_inputs(5), torch)
@@ -185,6 +186,14 @@ def kernel_pass(torch, fa, fi, reps=3):
         fa.forward(q, k, v, causal=True, out=o, lse=lse)
         fa.backward_stages(q, k, v, o, do, lse, dq, dk, dv, dvec, causal=True)
         fa.backward(q, k, v, o, do, lse, causal=True, dq=dq, dk=dk, dv=dv)
+    # the variants on the step's shape: dropout (p = 0.1) and block-sparse (blocks kept with
+    # p = 1/4 plus the diagonal), as bench.py times them
+    bmask = torch.from_numpy(fi.block_mask(B, H, N // 128, 0.25, 5)).cuda()
+    for _ in range(reps):
+        fa.forward(q, k, v, causal=True, out=o, lse=lse, p_drop=0.1, seed=1234)
+        fa.backward(q, k, v, o, do, lse, causal=True, p_drop=0.1, seed=1234, dq=dq, dk=dk, dv=dv)
+        fa.forward_blocksparse(q, k, v, bmask, causal=True, out=o, lse=lse)
+        fa.backward_blocksparse(q, k, v, o, do, lse, bmask, causal=True, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     del q3, k3, v3, o3, l3
     q4, k4, v4, _ = _upload(fi.workload_inputs(4), torch)

@@ -200,6 +200,12 @@ STALL_KERNELS = (
     ("dK/dV (wave pairs)", "bwd_dkdv_pair_kernel<Bf16, 128, true, false, false, false>", 524288, 2 * _F5),
     ("dQ, computing D (in fattn_bwd)", "bwd_dq_kernel<Bf16, 128, true, false, false, false, true>", 262144, 1.5 * _F5),
     ("dQ, D given (stage entry point)", "bwd_dq_kernel<Bf16, 128, true, false, false, false, false>", 262144, 1.5 * _F5),
+    ("forward, dropout p = 0.1", "fwd_kernel<Bf16, 128, 256, 128, 2, true, false, true, false>", 262144, _F5),
+    ("dK/dV, dropout p = 0.1", "bwd_dkdv_pair_kernel<Bf16, 128, true, false, true, false>", 524288, 2 * _F5),
+    ("dQ, dropout p = 0.1", "bwd_dq_kernel<Bf16, 128, true, false, true, false, true>", 262144, 1.5 * _F5),
+    ("forward, block-sparse", "fwd_kernel<Bf16, 128, 128, 64, 2, true, false, false, true>", 262144, 0.0),
+    ("dK/dV, block-sparse", "bwd_dkdv_pair_kernel<Bf16, 128, true, false, false, true>", 524288, 0.0),
+    ("dQ, block-sparse", "bwd_dq_kernel<Bf16, 128, true, false, false, true, true>", 262144, 0.0),
 )
 
 
