@@ -58,6 +58,9 @@ def _compile(src, hipcc, extra, verbose):
 
 MICROBENCH = os.path.join(HERE, "microbench")
 TOOLS = ["issue_rates.hip", "atomic_rates.hip"]  # stand-alone measurement programs, on request
+# measurement libraries, on request: the one-wave forward ablation keeps its MFMA results in AGPRs,
+# so it is built without the VGPR-form flag
+TOOL_LIBS = ["fwd_one_wave.hip"]
 
 
 def _build_tool(src, hipcc, verbose):
@@ -69,6 +72,18 @@ def _build_tool(src, hipcc, verbose):
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}{r.stderr}")
     os.replace(exe + ".tmp", exe)
+
+
+def _build_tool_lib(src, hipcc, verbose):
+    out = os.path.join(MICROBENCH, "lib" + os.path.splitext(src)[0] + ".so")
+    flags = [c for c in COMMON if c not in ("-mllvm", "-amdgpu-mfma-vgpr-form")]
+    cmd = [hipcc, *flags, "-shared", os.path.join(MICROBENCH, src), "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}{r.stderr}")
+    os.replace(out + ".tmp", out)
 
 
 def build(verbose: bool = False, resource_usage: bool = False, tools: bool = False) -> str:
@@ -90,6 +105,9 @@ def build(verbose: bool = False, resource_usage: bool = False, tools: bool = Fal
         for src in TOOLS:
             if os.path.exists(os.path.join(MICROBENCH, src)):
                 _build_tool(src, hipcc, verbose)
+        for src in TOOL_LIBS:
+            if os.path.exists(os.path.join(MICROBENCH, src)):
+                _build_tool_lib(src, hipcc, verbose)
     return OUT
 
 

@@ -81,7 +81,7 @@ def source_hash() -> str:
 def short_name(kernel: str) -> str:
     k = kernel.replace("fattn::(anonymous namespace)::", "").replace("fattn::", "")
     k = k.replace("(unsigned short const*, unsigned short const*, float*, long long)", "")
-    for args in ("FwdArgs", "BwdArgs", "SplitArgs", "CombineArgs", "KoArgs"):
+    for args in ("FwdArgs", "BwdArgs", "SplitArgs", "CombineArgs", "KoArgs", "OwArgs"):
         k = k.replace(f"((anonymous namespace)::{args})", "")
     return k.replace("void ", "").strip()
 
@@ -209,13 +209,29 @@ STALL_KERNELS = (
 )
 
 
-def stall_table(run_dir, peak_tflops=2516.6, max_mhz=2400.0):
+# The one-wave-per-SIMD forward ablation (microbench/fwd_one_wave.py, after build --tools) beside
+# the library forward, on the B=4 H=16 N=4096 d=128 causal prefill.
+ONE_WAVE_KERNELS = (
+    ("library forward (two waves per SIMD)", "fwd_kernel<Bf16, 128, 256, 128, 2, true, false, false, false>",
+     524288, 2 * _F5),
+    ("one wave per SIMD, compiler order", "fwd_one_wave_kernel<Bf16, 3, true, 0>", 262144, 2 * _F5),
+    ("one wave per SIMD, fixed slots", "fwd_one_wave_kernel<Bf16, 3, true, 1>", 262144, 2 * _F5),
+    ("one wave per SIMD, fixed slots, 4 stages", "fwd_one_wave_kernel<Bf16, 4, true, 1>", 262144, 2 * _F5),
+)
+ONE_WAVE_COMMANDS = {
+    key: "rocprofv3 --pmc " + ctrs + " --output-format csv -d {run}/" + key + " -o run -- "
+         "python -u io_aware_tiled_fattn_amd/microbench/fwd_one_wave.py --timing-only"
+    for key, ctrs in STALL_COUNTERS.items()
+}
+
+
+def stall_table(run_dir, peak_tflops=2516.6, max_mhz=2400.0, kernels=None):
     """Per step kernel: time, engine clock, MFMA busy, and where the waves' cycles go, from the
     two SQ counter passes (STALL_COMMANDS)."""
     d1 = _per_dispatch(_find(run_dir, "sq1", "counter_collection.csv"))
     d2 = _per_dispatch(_find(run_dir, "sq2", "counter_collection.csv"))
     rows = []
-    for label, sig, grid, flops in STALL_KERNELS:
+    for label, sig, grid, flops in (kernels or STALL_KERNELS):
         a = [v for v in d1.values() if v["kernel"].startswith(sig) and v["grid"] == grid]
         b = [v for v in d2.values() if v["kernel"].startswith(sig) and v["grid"] == grid]
         if not a or not b:
@@ -249,18 +265,20 @@ def stall_table(run_dir, peak_tflops=2516.6, max_mhz=2400.0):
     return rows
 
 
-def write_stalls(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
+def write_stalls(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16", kernels=None, commands=None,
+                 title=None, runs_note=None, name=None):
     os.makedirs(prof_dir, exist_ok=True)
-    rows = stall_table(run_dir)
+    rows = stall_table(run_dir, kernels=kernels)
     pct = lambda x: "—" if x is None else f"{x:.1%}"
     num = lambda x, f="{:.2f}": "—" if x is None else f.format(x)
-    lines = [f"# Where the step kernels' cycles go — {workload} (and the B=4 prefill forward)\n",
+    title = title or f"Where the step kernels' cycles go — {workload} (and the B=4 prefill forward)"
+    runs_note = runs_note or ("Every figure is the mean over the kernel's launches in the pass (bench.py "
+                              "--kernel-pass runs each three times after 0.5 s of warm-up).")
+    lines = [f"# {title}\n",
              "Commands (from the repository root, on the GPU box; RUN is an output folder):\n"]
     for key in ("sq1", "sq2"):
-        lines.append("    " + STALL_COMMANDS[key].format(run="RUN"))
-    lines += ["",
-              "Every figure is the mean over the kernel's launches in the pass (bench.py --kernel-pass "
-              "runs each three times after 0.5 s of warm-up).",
+        lines.append("    " + (commands or STALL_COMMANDS)[key].format(run="RUN"))
+    lines += ["", runs_note,
               "- Engine clock = GRBM_GUI_ACTIVE / 8 XCDs / kernel duration (the counter runs at the "
               "engine clock and is summed over the XCDs). The nominal peak (2516.6 TFLOP/s) assumes "
               "2400 MHz; the clock-adjusted fraction divides by the peak at the measured clock.",
@@ -286,9 +304,22 @@ def write_stalls(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
         lines.append(f"| {r['label']} | {pct(r['issuing'])} | {pct(r['wait_any'])} | {pct(r['wait_issue'])} | "
                      f"{pct(r['valu_active'])} | {pct(r['lds_active'])} | {pct(r['lds_wait'])} | "
                      f"{num(r['valu_per_mfma'])} | {num(r['lds_per_mfma'])} | {num(r['salu_per_mfma'])} |")
-    with open(os.path.join(prof_dir, f"stalls_{workload}.md"), "w") as f:
+    with open(os.path.join(prof_dir, name or f"stalls_{workload}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     return rows
+
+
+def write_one_wave(run_dir, prof_dir):
+    """Counter summary of the one-wave forward ablation beside the library forward."""
+    return write_stalls(
+        run_dir, prof_dir, kernels=ONE_WAVE_KERNELS, commands=ONE_WAVE_COMMANDS,
+        title="One wave per SIMD against two: forward B=4 H=16 N=4096 d=128 causal bf16",
+        runs_note=("Every figure is the mean over the kernel's launches in the pass (fwd_one_wave.py "
+                   "--timing-only runs each variant 155 times per shape after 0.5 s of warm-up; only "
+                   "the B=4 launches are listed). In the one-wave kernels a SIMD holds one wave, so "
+                   "'waiting for an issue slot' there is time the wave's next instruction waits for "
+                   "its own unit (MFMA, VALU, LDS) to accept it."),
+        name="stalls_fwd_one_wave_b4h16n4096d128_causal_bf16.md")
 
 
 def _is_decode(kernel):
@@ -491,6 +522,10 @@ if __name__ == "__main__":
             with open(sys.argv[4]) as f:
                 times = json.loads(f.read().strip().splitlines()[-1])["runs"]
         for r in write_sweep(sys.argv[2], sys.argv[3], times):
+            print(r)
+        sys.exit(0)
+    if sys.argv[1] == "onewave":
+        for r in write_one_wave(sys.argv[2], sys.argv[3]):
             print(r)
         sys.exit(0)
     if sys.argv[1] == "stalls":
