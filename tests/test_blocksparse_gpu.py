@@ -72,6 +72,39 @@ def test_blocksparse_all_ones_is_the_dense_kernel(d, causal):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def _tilted(N, d, seed, kind):
+    """bf16 inputs whose logits get a large per-key offset through Q[..., 0] = 1 and K[..., 0]:
+    'rising' adds 0.04 per key, 'alternate' adds 30 to the keys of every other 64-key tile. Either
+    way the running maximum outgrows the forward's slack on many of the tiles a row visits, so the
+    rescale path runs between skipped and visited tiles."""
+    inp = fi.make_inputs((1, 2, N, d), "bf16", seed)
+    scale = 1 / math.sqrt(d)
+    q, k = inp.q.copy(), inp.k.copy()
+    q[..., 0] = 1.0
+    j = np.arange(N, dtype=np.float32)
+    off = 0.04 * j if kind == "rising" else 30.0 * ((np.arange(N) // 64) % 2).astype(np.float32)
+    k[..., 0] = off / np.float32(scale)
+    q, qb = fi.round_bits(q, "bf16")
+    k, kb = fi.round_bits(k, "bf16")
+    bits = dict(inp.bits)
+    bits["q"], bits["k"] = qb, kb
+    return fi.Inputs("bf16", q, k, inp.v, None, bits), scale
+
+
+@pytest.mark.parametrize("kind", ["rising", "alternate"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("density", [1.0, 0.5])
+def test_blocksparse_tilted_logits(kind, causal, density):
+    N, d = 1000, 128
+    log(f"blocksparse tilted logits kind={kind} causal={causal} density={density}")
+    inp, scale = _tilted(N, d, 1300, kind)
+    nb = (N + 127) // 128
+    mask = fi.block_mask(1, 2, nb, density, 1301, diagonal=True)
+    o, lse = _run(inp, mask, causal)
+    o_ref, lse_ref = obs.forward(inp.q, inp.k, inp.v, scale, mask, causal)
+    _check(o, lse, o_ref, lse_ref, "bf16")
+
+
 def test_blocksparse_empty_mask_and_single_block():
     import torch
     fa = _fa()
