@@ -91,9 +91,10 @@ int fattn_fwd_tiled(const void* q, const void* k, const void* v, void* o, float*
  * whether the result changes, names dropout as a training-time source of difference; the pages
  * fix no convention, so this one is stated here). With P = softmax(S) and keep mask M:
  *     O = ((P * M) / (1 - p_drop)) V,   LSE = the undropped statistic (as fattn_fwd writes it).
- * M(b, h, i, j) = 1 iff x >= floor(p_drop * 2^32), where x is word j % 4 of Philox4x32-10 (Salmon
- * et al., SC 2011) at counter (j / 4, i, b*H + h, 0) with key (seed mod 2^32, seed / 2^32). The
- * same (seed, p_drop) reproduces the same mask in fattn_bwd_dropout. p_drop in [0, 1), else
+ * M(b, h, i, j) = 1 iff x >= floor(p_drop * 2^16), where x is 16-bit field f = j % 8 of
+ * Philox4x32-10 (Salmon et al., SC 2011) at counter (j / 8, i, b*H + h, 0) with key
+ * (seed mod 2^32, seed / 2^32): the low half of output word f for f < 4, the high half of word
+ * f - 4 otherwise. The same (seed, p_drop) reproduces the same mask in fattn_bwd_dropout. p_drop in [0, 1), else
  * FATTN_ERR_DROPOUT; p_drop = 0 is fattn_fwd. f16/bf16 only; uses the default tile shape.
  */
 int fattn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,

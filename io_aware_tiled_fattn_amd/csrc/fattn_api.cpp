@@ -30,13 +30,14 @@ int check_common(int B, int H, int N, int d, int dtype) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? FATTN_OK : FATTN_ERR_LAUNCH; }
 
-// Keep threshold floor(p 2^32) and 1 / (1 - p) of a drop probability p in (0, 1).
+// Keep threshold floor(p 2^16) of a 16-bit generator field and 1 / (1 - p), for a drop
+// probability p in [0, 1).
 fattn::DropParams drop_params(float p, unsigned long long seed) {
   fattn::DropParams d;
   d.seed_lo = (uint32_t)(seed & 0xffffffffull);
   d.seed_hi = (uint32_t)(seed >> 32);
-  const double t = std::floor((double)p * 4294967296.0);
-  d.thr = t >= 4294967295.0 ? 0xffffffffu : (uint32_t)t;
+  const double t = std::floor((double)p * 65536.0);
+  d.thr = t >= 65535.0 ? 65535u : (uint32_t)t;
   d.inv_keep = (float)(1.0 / (1.0 - (double)p));
   return d;
 }

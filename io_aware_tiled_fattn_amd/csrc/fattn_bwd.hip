@@ -391,12 +391,9 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
             } else {
               // B gets P with the sign bit marking a dropped element (P >= 0, so the sign is
               // free): it then needs no generator of its own; dV takes P M / (1 - p)
-              const uint32_t kb = quad_keep_bits((uint32_t)key >> 2, (uint32_t)(q_base + qb * 32 + 8 * (2 * half) + 4 * h),
-                                                 (uint32_t)bh, a.drop, lane);
-              const uint32_t kb2 = quad_keep_bits((uint32_t)key >> 2,
-                                                  (uint32_t)(q_base + qb * 32 + 8 * (2 * half + 1) + 4 * h),
+              // bit e: this lane's key for query q_base + 32 qb + 8 (2 half + e / 4) + 4h + e % 4
+              const uint32_t bits = col_keep_bits((uint32_t)key >> 3, (uint32_t)(q_base + qb * 32 + 16 * half + 4 * h),
                                                   (uint32_t)bh, a.drop, lane);
-              const uint32_t bits = kb | (kb2 << 4);
               u32x4 ps;
 #pragma unroll
               for (int e2 = 0; e2 < 4; ++e2) {
@@ -695,21 +692,17 @@ __global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)
       vec8 dsp[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        u32x4 wd[2];
-        if (DROP) {
-#pragma unroll
-          for (int g = 0; g < 2; ++g)
-            wd[g] = philox4x32_10((uint32_t)(k0 / 4 + 8 * kb + 2 * (2 * half + g) + h), (uint32_t)qrow,
-                                  (uint32_t)bh, 0u, a.drop.seed_lo, a.drop.seed_hi);
-        }
+        // element 8 half + t holds key 4h + (t % 4) of 8-key group k0 / 8 + 4 kb + 2 half + t / 4
+        uint32_t kf[8];
+        if (DROP) row_keep_fields((uint32_t)(k0 / 8 + 4 * kb + 2 * half), (uint32_t)qrow, (uint32_t)bh, a.drop, h, kf);
         u32x4 packed;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const int e = 8 * half + 2 * e2;
           float dp0 = dp[e], dp1 = dp[e + 1];
           if (DROP) {
-            dp0 = wd[e2 >> 1][2 * (e2 & 1)] >= a.drop.thr ? dp0 * a.drop.inv_keep : 0.f;
-            dp1 = wd[e2 >> 1][2 * (e2 & 1) + 1] >= a.drop.thr ? dp1 * a.drop.inv_keep : 0.f;
+            dp0 = kf[2 * e2] >= (a.drop.thr << 16) ? dp0 * a.drop.inv_keep : 0.f;
+            dp1 = kf[2 * e2 + 1] >= (a.drop.thr << 16) ? dp1 * a.drop.inv_keep : 0.f;
           }
           const float ds0 = __builtin_amdgcn_exp2f(s[e]) * (dp0 - dval);
           const float ds1 = __builtin_amdgcn_exp2f(s[e + 1]) * (dp1 - dval);

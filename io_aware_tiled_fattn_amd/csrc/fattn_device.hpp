@@ -158,30 +158,69 @@ __device__ inline u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uin
   return u32x4{c0, c1, c2, c3};
 }
 
-// The keep decision of (head bh, query i, key j) is word j % 4 of Philox4x32-10 at counter
-// (j / 4, i, bh, 0) under the 64-bit seed, compared with floor(p 2^32).
+// The keep decision of (head bh, query i, key j) is 16-bit field f = j % 8 of Philox4x32-10 at
+// counter (j / 8, i, bh, 0) under the 64-bit seed (field f: the low half of word f for f < 4, the
+// high half of word f - 4 otherwise), compared with floor(p 2^16). One generator call thus
+// decides 8 keys of one query.
 struct DropParams {
   uint32_t seed_lo, seed_hi;
-  uint32_t thr;      // floor(p * 2^32)
+  uint32_t thr;      // floor(p * 2^16)
   float inv_keep;    // 1 / (1 - p)
 };
 
-// Keep bits of 4 consecutive keys of one key group (held by the 4 lanes of a quad, one key per
-// lane, key % 4 = lane % 4) for the 4 consecutive queries q4 .. q4 + 3: every lane draws the
-// generator for one query (q4 + lane % 4), turns its 4 words into a 4-bit mask (bit r = key r),
-// and the quad exchanges the masks over DPP. Bit t of the result is the keep bit of this lane's
-// key for query q4 + t. Every lane of the quad must be active.
 template <int T>
 __device__ inline uint32_t quad_bcast(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, T | (T << 2) | (T << 4) | (T << 6), 0xF, 0xF, false);
 }
-__device__ inline uint32_t quad_keep_bits(uint32_t kgroup, uint32_t q4, uint32_t bh, const DropParams& dp, int lane) {
-  const u32x4 w = philox4x32_10(kgroup, q4 + (uint32_t)(lane & 3), bh, 0u, dp.seed_lo, dp.seed_hi);
-  const uint32_t m = (w[0] >= dp.thr ? 1u : 0u) | (w[1] >= dp.thr ? 2u : 0u) | (w[2] >= dp.thr ? 4u : 0u) |
-                     (w[3] >= dp.thr ? 8u : 0u);
-  const uint32_t r = (uint32_t)(lane & 3);
-  return ((quad_bcast<0>(m) >> r) & 1u) | (((quad_bcast<1>(m) >> r) & 1u) << 1) |
-         (((quad_bcast<2>(m) >> r) & 1u) << 2) | (((quad_bcast<3>(m) >> r) & 1u) << 3);
+
+// Row layout (forward and dQ kernels: lanes l and l ^ 32 own the same query row, lane half h
+// holds keys 4h .. 4h + 3 of every 8-key group). For the two 8-key groups g8 and g8 + 1, lane
+// half h draws the generator once, for group g8 + h, and the two halves swap the 16-bit fields the
+// other one needs. On return f[4g + r] holds, in its high 16 bits, the field of key
+// 8 (g8 + g) + 4h + r of this lane's row (the low bits are not defined): the key is kept iff
+// f[4g + r] >= dp.thr << 16. Both lanes of every pair must be active.
+__device__ inline void row_keep_fields(uint32_t g8, uint32_t row, uint32_t bh, const DropParams& dp, int h,
+                                       uint32_t (&f)[8]) {
+  const u32x4 w = philox4x32_10(g8 + (uint32_t)h, row, bh, 0u, dp.seed_lo, dp.seed_hi);
+  const uint32_t sh_own = 16u - 16u * (uint32_t)h, sh_send = 16u * (uint32_t)h;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t own = w[r] << sh_own;    // field 4h + r of the drawn group, moved to the top
+    const uint32_t send = w[r] << sh_send;  // field 4(1 - h) + r: the partner's key
+    // v_permlane32_swap of a value with itself leaves {low half's, high half's} value in the two
+    // results; xor-ing both with the lane's own value leaves the partner's, whichever order
+    const auto sw = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+    const uint32_t got = sw[0] ^ sw[1] ^ send;
+    f[r] = h ? got : own;  // group g8 (drawn by the h = 0 lane)
+    f[4 + r] = h ? own : got;
+  }
+}
+
+// Column layout (dK/dV kernel: a lane owns one key, key % 8 = lane % 8, so the 8 lanes of an
+// octet hold one 8-key group g8; lane half h owns queries 4h + r of each 8-query block). Octet
+// lane t draws the generator once, for query q0 + 8 (t / 4) + (t % 4), and turns its 8 fields
+// into an 8-bit mask (bit k = key k of the group); the octet then transposes the 8 x 8 bits over
+// DPP (the other quad's masks arrive by a half-row mirror, then quad broadcasts). Bit u of the
+// result is the keep bit of this lane's key for query q0 + 8 (u / 4) + (u % 4). Every lane of the
+// octet must be active.
+__device__ inline uint32_t col_keep_bits(uint32_t g8, uint32_t q0, uint32_t bh, const DropParams& dp, int lane) {
+  const int t = lane & 7;
+  const u32x4 w = philox4x32_10(g8, q0 + 8u * (uint32_t)(t >> 2) + (uint32_t)(t & 3), bh, 0u, dp.seed_lo, dp.seed_hi);
+  uint32_t m = 0u;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m |= ((w[r] & 0xffffu) >= dp.thr ? 1u : 0u) << r;
+    m |= ((w[r] >> 16) >= dp.thr ? 1u : 0u) << (r + 4);
+  }
+  // row_half_mirror: octet lane i receives lane 7 - i's mask, so quad lane v of this quad holds
+  // the other quad's lane 3 - v
+  const uint32_t oth = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, false);
+  uint32_t x = 0u, y = 0u;  // this quad's queries, the other quad's
+  x |= ((quad_bcast<0>(m) >> t) & 1u) | (((quad_bcast<1>(m) >> t) & 1u) << 1) |
+       (((quad_bcast<2>(m) >> t) & 1u) << 2) | (((quad_bcast<3>(m) >> t) & 1u) << 3);
+  y |= ((quad_bcast<3>(oth) >> t) & 1u) | (((quad_bcast<2>(oth) >> t) & 1u) << 1) |
+       (((quad_bcast<1>(oth) >> t) & 1u) << 2) | (((quad_bcast<0>(oth) >> t) & 1u) << 3);
+  return t < 4 ? (x | (y << 4)) : (y | (x << 4));
 }
 
 // ---- block-mask scans ------------------------------------------------------------------------

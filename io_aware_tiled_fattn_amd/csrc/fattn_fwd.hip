@@ -280,15 +280,11 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        // keys of elements 8 half + 4 g + r (g = 0, 1): key group (j BC + 32 kb + 8 (2 half + g)
-        // + 4 h) / 4, word r
-        u32x4 wd[2];
-        if (DROP) {
-#pragma unroll
-          for (int g = 0; g < 2; ++g)
-            wd[g] = philox4x32_10((uint32_t)((j * BC) / 4 + 8 * kb + 2 * (2 * half + g) + h), (uint32_t)qrow,
-                                  (uint32_t)bh, 0u, a.drop.seed_lo, a.drop.seed_hi);
-        }
+        // element 8 half + t (t = 4g + r) holds key j BC + 32 kb + 8 (2 half + g) + 4h + r, i.e.
+        // key 4h + r of 8-key group (j BC + 32 kb) / 8 + 2 half + g: keep bit t
+        uint32_t kf[8];
+        if (DROP)
+          row_keep_fields((uint32_t)((j * BC) / 8 + 4 * kb + 2 * half), (uint32_t)qrow, (uint32_t)bh, a.drop, h, kf);
         u32x4 packed;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
@@ -296,8 +292,8 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
           float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * e2 + 1], a.c, neg_m));
           ls += p0 + p1;
           if (DROP) {
-            p0 = wd[e2 >> 1][2 * (e2 & 1)] >= a.drop.thr ? p0 : 0.f;
-            p1 = wd[e2 >> 1][2 * (e2 & 1) + 1] >= a.drop.thr ? p1 : 0.f;
+            p0 = kf[2 * e2] >= (a.drop.thr << 16) ? p0 : 0.f;
+            p1 = kf[2 * e2 + 1] >= (a.drop.thr << 16) ? p1 : 0.f;
           }
           packed[e2] = TR::pack2(p0, p1);
         }

@@ -12,8 +12,10 @@ taken here:
 * The keep decision for (head bh = b*H + h, query row i, key j) comes from the counter-based
   generator Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as
   1, 2, 3", SC 2011), which both this oracle and the kernels implement from its definition:
-  counter (j // 4, i, bh, 0), key (seed mod 2^32, seed // 2^32), output word j % 4 = x.
-  The key is kept iff x >= floor(p * 2^32), so P(keep) = 1 - p up to 2^-32.
+  counter (j // 8, i, bh, 0), key (seed mod 2^32, seed // 2^32). One call covers 8 keys with
+  16 bits each: key j takes field f = j % 8, the low half (f < 4) or the high half (f >= 4) of
+  output word f % 4, as x in [0, 2^16). The key is kept iff x >= floor(p * 2^16), so
+  P(keep) = 1 - p up to 2^-16.
 * Backward, by the chain rule through O = Pd V with Pd = P * M / (1 - p):
   dV = Pd^T dO;  dP = (dO V^T) * M / (1 - p);  D = rowsum(dO * O) (= rowsum(P * dP));
   dS = P * (dP - D);  dQ = scale dS K;  dK = scale dS^T Q.
@@ -67,20 +69,27 @@ def philox4x32_10_np(c0, c1, c2, c3, k0, k1):
 
 
 def threshold(p):
-    """Integer threshold floor(p * 2^32) of drop probability p in [0, 1)."""
+    """Integer threshold floor(p * 2^16) of drop probability p in [0, 1)."""
     p = float(np.float32(p))
     if not (0.0 <= p < 1.0):
         raise ValueError("drop probability must be in [0, 1)")
-    return int(np.floor(p * 4294967296.0))
+    return int(np.floor(p * 65536.0))
+
+
+def keep_field(words, j):
+    """The 16-bit field of key j (j % 8) in the 4 output words of its call."""
+    f = int(j) % 8
+    return (int(words[f % 4]) >> (16 * (f // 4))) & 0xFFFF
 
 
 def keep_mask(seed, p, bh, rows, keys):
     """Boolean keep mask [len(rows), len(keys)] of head bh."""
     rows = np.asarray(rows, np.int64)[:, None]
     keys = np.asarray(keys, np.int64)[None, :]
-    words = philox4x32_10_np(keys >> 2, rows, bh, 0, seed & MASK32, (seed >> 32) & MASK32)
-    pick = (keys & 3)
-    x = np.where(pick == 0, words[0], np.where(pick == 1, words[1], np.where(pick == 2, words[2], words[3])))
+    words = philox4x32_10_np(keys >> 3, rows, bh, 0, seed & MASK32, (seed >> 32) & MASK32)
+    f = keys & 7
+    w = np.where((f & 3) == 0, words[0], np.where((f & 3) == 1, words[1], np.where((f & 3) == 2, words[2], words[3])))
+    x = (w >> (np.uint64(16) * (f >> 2).astype(np.uint64))) & np.uint64(0xFFFF)
     return x >= np.uint64(threshold(p))
 
 

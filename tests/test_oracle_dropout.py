@@ -46,14 +46,24 @@ def test_philox_vectorised_equals_scalar():
 
 
 def test_keep_mask_layout_and_rate():
-    # key j of row i takes word j % 4 of the generator at counter (j // 4, i, bh, 0)
+    # key j of row i takes 16-bit field j % 8 of the generator at counter (j // 8, i, bh, 0):
+    # fields 0..3 are the low halves of words 0..3, fields 4..7 their high halves
     seed = 0x0123456789ABCDEF
-    m = dr.keep_mask(seed, 0.5, 7, [3], np.arange(8))[0]
+    keys = np.arange(24)
     thr = dr.threshold(0.5)
-    for j in range(8):
-        w = dr.philox4x32_10((j // 4, 3, 7, 0), (seed & 0xFFFFFFFF, seed >> 32))[j % 4]
-        assert bool(m[j]) == (w >= thr)
-    assert thr == 2**31
+    assert thr == 2**15
+    for p in (0.5, 0.3):
+        m = dr.keep_mask(seed, p, 7, [3], keys)[0]
+        t = dr.threshold(p)
+        for j in keys:
+            w = dr.philox4x32_10((j // 8, 3, 7, 0), (seed & 0xFFFFFFFF, seed >> 32))
+            x = (w[j % 4] & 0xFFFF) if j % 8 < 4 else (w[j % 4] >> 16)
+            assert x == dr.keep_field(w, j)
+            assert bool(m[j]) == (x >= t)
+    # one call's 128 bits decide 8 keys: keys 8g .. 8g + 7 share a counter, the next 8 do not
+    w0 = dr.philox4x32_10((0, 3, 7, 0), (seed & 0xFFFFFFFF, seed >> 32))
+    w1 = dr.philox4x32_10((1, 3, 7, 0), (seed & 0xFFFFFFFF, seed >> 32))
+    assert [dr.keep_field(w0, j) for j in range(8)] != [dr.keep_field(w1, j) for j in range(8, 16)]
     # rate: binomial, 5 sigma
     for p in (0.1, 0.5, 0.9):
         mask = dr.keep_mask(1234, p, 0, np.arange(256), np.arange(4096))
