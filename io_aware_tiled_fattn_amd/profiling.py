@@ -281,7 +281,12 @@ def write_stalls(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16", kerne
     lines += ["", runs_note,
               "- Engine clock = GRBM_GUI_ACTIVE / 8 XCDs / kernel duration (the counter runs at the "
               "engine clock and is summed over the XCDs). The nominal peak (2516.6 TFLOP/s) assumes "
-              "2400 MHz; the clock-adjusted fraction divides by the peak at the measured clock.",
+              "2400 MHz; the clock-adjusted fraction divides by the peak at the measured clock. The "
+              "counter also runs through each dispatch's own set-up: the 12 us rowsum kernel of the "
+              "same passes reads as 3.8 GHz, so some 18 to 28 thousand cycles per dispatch are not "
+              "kernel time. The clock of a 130-280 us kernel therefore reads 3-10% high (the "
+              "clock-adjusted fractions are lower bounds), and the 57-110 us block-sparse kernels "
+              "read above the 2400 MHz maximum.",
               "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles); co-issue = "
               "SQ_VALU_MFMA_COEXEC_CYCLES (a VALU instruction issued while the MFMA unit was busy) on "
               "the same base.",
