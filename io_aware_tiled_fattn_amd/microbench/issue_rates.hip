@@ -1,5 +1,6 @@
 // Issue-rate micro-benchmark for gfx950: how many SIMD cycles one wave64 instruction of each kind
-// occupies (bf16 MFMA 32x32x16, v_exp_f32, v_fma_f32, ds_read_b128, ds_read_b64_tr_b16), and how
+// occupies (bf16 MFMA 32x32x16, v_exp_f32, v_fma_f32, v_mad_u64_u32, v_bitop3_b32, ds_read_b128,
+// ds_read_b64_tr_b16, and a whole Philox4x32-10 call of the dropout kernels), and how
 // well MFMA overlaps VALU work from the same wave and from another wave on the same SIMD. These
 // are the ceilings the attention kernels work against: per score element the forward issues
 // 2 x 2d / 32768 MFMAs, one v_exp_f32 and a handful of plain VALU instructions.
@@ -36,7 +37,8 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int R = 2048;
 constexpr int LDS_BYTES = 65536;
 
-enum : int { LDS128 = 1, LDSTR = 2, MFMA = 4, EXP = 8, FMA = 16, LDSBW = 32, LDSTRBW = 64 };
+enum : int { LDS128 = 1, LDSTR = 2, MFMA = 4, EXP = 8, FMA = 16, LDSBW = 32, LDSTRBW = 64, MAD64 = 128, BOP3 = 256,
+             PHILOX = 1024 };
 
 // MODE: a bit set of the instruction groups each iteration issues; SPLIT: waves 0-3 issue only the
 // MFMA group and waves 4-7 only the VALU groups (so each SIMD pairs one MFMA wave with one VALU wave).
@@ -87,6 +89,42 @@ __global__ __launch_bounds__(512) void mix(float* out, long long* cyc, float see
                    (lds_i16x4*)(sm + ((lane * 8 + i * 512 + r * 64) & (LDS_BYTES - 1))))).x;
 #pragma unroll
       for (int i = 0; i < 16; ++i) x[i & 3] ^= y[i];
+    }
+    if ((MODE & MAD64) && do_valu) {  // 32 v_mad_u64_u32 in 8 independent chains
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint64_t pr = (uint64_t)0xD2511F53u * (uint32_t)__float_as_uint(fv[e]) + (uint32_t)__float_as_uint(fv[e + 8]);
+          fv[e] = __uint_as_float((uint32_t)(pr >> 32));
+          fv[e + 8] = __uint_as_float((uint32_t)pr);
+        }
+    }
+    if ((MODE & BOP3) && do_valu) {  // 64 v_bitop3 in 16 chains
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+  #pragma unroll
+        for (int e = 0; e < 16; ++e)
+          fv[e] = __uint_as_float(__builtin_amdgcn_bitop3_b32(__float_as_uint(fv[e]), (uint32_t)lane, (uint32_t)(e + k), 0x96));
+    }
+    if ((MODE & PHILOX) && do_valu) {  // 4 Philox4x32-10 calls (independent)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint32_t c0 = __float_as_uint(fv[4 * c]), c1 = __float_as_uint(fv[4 * c + 1]), c2 = __float_as_uint(fv[4 * c + 2]), c3 = __float_as_uint(fv[4 * c + 3]);
+        uint32_t k0 = 0x12345u + (uint32_t)r, k1 = 0x6789u;
+  #pragma unroll
+        for (int rr = 0; rr < 10; ++rr) {
+          const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+          const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+          c0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+          c1 = (uint32_t)p1;
+          c2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
+          c3 = (uint32_t)p0;
+          k0 += 0x9E3779B9u;
+          k1 += 0xBB67AE85u;
+        }
+        fv[4 * c] = __uint_as_float(c0); fv[4 * c + 1] = __uint_as_float(c1); fv[4 * c + 2] = __uint_as_float(c2); fv[4 * c + 3] = __uint_as_float(c3);
+      }
     }
     if (do_mfma) {  // 16 MFMAs in 4 independent accumulator chains
 #pragma unroll
@@ -180,5 +218,11 @@ int main() {
   rc |= run<LDSBW, false>("16 x ds_read_b128, independent", 512, 32, out, cyc, B);
   rc |= run<LDSTRBW, false>("16 x ds_read_b64_tr_b16, independent", 512, 32, out, cyc, B);
   rc |= run<MFMA | LDSBW, false>("16 mfma + 16 b128 reads, same wave", 512, 32, out, cyc, B);
+  // the dropout generator: 32 x 32 -> 64-bit products, three-input xors, and whole calls
+  rc |= run<MAD64, false>("32 x v_mad_u64_u32", 512, 64, out, cyc, B);
+  rc |= run<BOP3, false>("64 x v_bitop3_b32", 512, 128, out, cyc, B);
+  rc |= run<PHILOX, false>("4 x philox4x32-10 (units: calls)", 512, 8, out, cyc, B);
+  rc |= run<MFMA | PHILOX, false>("16 mfma + 4 philox, same wave", 512, 32, out, cyc, B);
+  rc |= run<MFMA | PHILOX, true>("16 mfma (waves 0-3) / 4 philox (waves 4-7)", 512, 16, out, cyc, B);
   return rc;
 }
