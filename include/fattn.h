@@ -56,7 +56,7 @@ typedef enum {
   FATTN_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned */
   FATTN_ERR_SCALE = -7,       /* scale is NaN or infinite */
   FATTN_ERR_WORKSPACE = -8,   /* workspace NULL or smaller than fattn_bwd_workspace_size() */
-  FATTN_ERR_UNSUPPORTED = -9, /* a valid request this build does not implement */
+  FATTN_ERR_UNSUPPORTED = -9, /* a valid request the library does not implement */
   FATTN_ERR_LAUNCH = -10,     /* the HIP runtime rejected a kernel launch */
   FATTN_ERR_ALIAS = -11,      /* an output pointer equals an input pointer */
   FATTN_ERR_CAUSAL = -12,     /* causal not 0 or 1 */

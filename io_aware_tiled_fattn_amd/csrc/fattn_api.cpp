@@ -98,7 +98,7 @@ const char* fattn_strerror(int status) {
     case FATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
     case FATTN_ERR_SCALE: return "scale is not finite";
     case FATTN_ERR_WORKSPACE: return "workspace missing or too small";
-    case FATTN_ERR_UNSUPPORTED: return "not implemented in this build";
+    case FATTN_ERR_UNSUPPORTED: return "not implemented in this library";
     case FATTN_ERR_LAUNCH: return "kernel launch failed";
     case FATTN_ERR_ALIAS: return "an output aliases an input";
     case FATTN_ERR_CAUSAL: return "causal must be 0 or 1";

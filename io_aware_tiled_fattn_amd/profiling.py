@@ -265,8 +265,15 @@ def stall_table(run_dir, peak_tflops=2516.6, max_mhz=2400.0, kernels=None):
     return rows
 
 
+STEP_CLOCK_NOTE = ("The counter also runs through each dispatch's own set-up: the 12 us rowsum kernel of "
+                   "the same passes reads as 3.8 GHz, so some 18 to 28 thousand cycles per dispatch are "
+                   "not kernel time. The clock of a 130-280 us kernel therefore reads 3-10% high (the "
+                   "clock-adjusted fractions are lower bounds), and the 57-110 us block-sparse kernels "
+                   "read above the 2400 MHz maximum.")
+
+
 def write_stalls(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16", kernels=None, commands=None,
-                 title=None, runs_note=None, name=None):
+                 title=None, runs_note=None, name=None, clock_note=STEP_CLOCK_NOTE):
     os.makedirs(prof_dir, exist_ok=True)
     rows = stall_table(run_dir, kernels=kernels)
     pct = lambda x: "—" if x is None else f"{x:.1%}"
@@ -275,18 +282,14 @@ def write_stalls(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16", kerne
     runs_note = runs_note or ("Every figure is the mean over the kernel's launches in the pass (bench.py "
                               "--kernel-pass runs each three times after 0.5 s of warm-up).")
     lines = [f"# {title}\n",
-             "Commands (from the repository root, on the GPU box; RUN is an output folder):\n"]
+             "Commands (from the repository root, on an MI355X; RUN is an output folder):\n"]
     for key in ("sq1", "sq2"):
         lines.append("    " + (commands or STALL_COMMANDS)[key].format(run="RUN"))
     lines += ["", runs_note,
               "- Engine clock = GRBM_GUI_ACTIVE / 8 XCDs / kernel duration (the counter runs at the "
               "engine clock and is summed over the XCDs). The nominal peak (2516.6 TFLOP/s) assumes "
-              "2400 MHz; the clock-adjusted fraction divides by the peak at the measured clock. The "
-              "counter also runs through each dispatch's own set-up: the 12 us rowsum kernel of the "
-              "same passes reads as 3.8 GHz, so some 18 to 28 thousand cycles per dispatch are not "
-              "kernel time. The clock of a 130-280 us kernel therefore reads 3-10% high (the "
-              "clock-adjusted fractions are lower bounds), and the 57-110 us block-sparse kernels "
-              "read above the 2400 MHz maximum.",
+              "2400 MHz; the clock-adjusted fraction divides by the peak at the measured clock. "
+              + clock_note,
               "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles); co-issue = "
               "SQ_VALU_MFMA_COEXEC_CYCLES (a VALU instruction issued while the MFMA unit was busy) on "
               "the same base.",
@@ -324,7 +327,10 @@ def write_one_wave(run_dir, prof_dir):
                    "the B=4 launches are listed). In the one-wave kernels a SIMD holds one wave, so "
                    "'waiting for an issue slot' there is time the wave's next instruction waits for "
                    "its own unit (MFMA, VALU, LDS) to accept it."),
-        name="stalls_fwd_one_wave_b4h16n4096d128_causal_bf16.md")
+        name="stalls_fwd_one_wave_b4h16n4096d128_causal_bf16.md",
+        clock_note=("The counter also runs through each dispatch's own set-up (some 18 to 28 thousand "
+                    "cycles, measured on the step kernels' passes), so the clocks of these 250-360 us "
+                    "kernels read 2-5% high."))
 
 
 def _is_decode(kernel):
@@ -371,7 +377,7 @@ def write_summaries(run_dir, prof_dir, workload="b2h16n4096d128_causal_bf16"):
     busy = mfma_busy(run_dir)
     for t in tr:
         t["mfma_busy"] = busy.get((t["kernel"], t["grid"])) if busy else None
-    cmd_note = "Commands (from the repository root, on the GPU box; RUN is an output folder):\n\n"
+    cmd_note = "Commands (from the repository root, on an MI355X; RUN is an output folder):\n\n"
     titles = {
         workload: (f"bench.py step workload ({workload}), the B=4 forward and the K-outer ablation",
                    "The forward kernel's calls mix the B=2 (step), B=4 (prefill, every tile) and "
@@ -455,7 +461,7 @@ def write_sweep(run_dir, prof_dir, times=None, bh=16, d=128):
                      "mfma_busy": mfma.get((t["kernel"], t["grid"]))})
     rows.sort(key=lambda r: (r["causal"], r["N"]))
     lines = ["# HBM bytes versus N — forward and backward, B=1 H=16 d=128 bf16\n",
-             "Commands (from the repository root, on the GPU box; RUN is an output folder):\n"]
+             "Commands (from the repository root, on an MI355X; RUN is an output folder):\n"]
     for key in ("fetch", "write", "mfma"):
         lines.append("    " + SWEEP_COMMANDS[key].format(run="RUN"))
     lines += ["", f"Counters calibrated on a 256 MiB + 256 MiB copy (FETCH_SIZE x{fc:.3f}, WRITE_SIZE x{wc:.3f}). "
