@@ -57,7 +57,7 @@ def _compile(src, hipcc, extra, verbose):
 
 
 MICROBENCH = os.path.join(HERE, "microbench")
-TOOLS = ["issue_rates.hip", "atomic_rates.hip"]  # stand-alone measurement programs, on request
+TOOLS = ["issue_rates.hip", "atomic_rates.hip", "stream_rates.hip"]  # stand-alone measurement programs, on request
 # measurement libraries, on request: the one-wave forward ablation keeps its MFMA results in AGPRs,
 # so it is built without the VGPR-form flag
 TOOL_LIBS = ["fwd_one_wave.hip"]
