@@ -481,9 +481,9 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
 // the K tile through the transposed read. K and V tiles of 64 keys stream memory -> LDS, two
 // stages deep.
 
-template <int D>
+template <int D, int BQ_ = 256>
 struct DqCfg {
-  static constexpr int BQ = 256;              // queries per work-group (32 per wave)
+  static constexpr int BQ = BQ_;              // queries per work-group (32 per wave)
   static constexpr int BK = 64;               // keys per step
   static constexpr int NT = BQ / 32 * 64;
   static constexpr int CPR = D / 8;
@@ -494,15 +494,14 @@ struct DqCfg {
 };
 
 // DROP: dS = P (dO V^T M / (1 - p) - D).
-// SPARSE: block-sparse attention over 128 x 128 (query, key) blocks: the work-group loads the key
-// tiles whose mask column is set for either of its two mask rows, and each wave computes the ones
-// its own mask row allows.
+// SPARSE: block-sparse attention over 128 x 128 (query, key) blocks: a work-group of 128 queries
+// (4 waves) is one mask row and loads and computes only the key tiles that row allows.
 // WITH_D: compute D = rowsum(dO * O) of the wave's rows here (from the dO fragments already in
 // registers and the O rows) instead of reading it, and write it for the dK/dV kernel; the result
 // is the preprocess kernel's bit for bit (same chunk sums, same pairing tree).
 template <typename TR, int D, bool CAUSAL, bool BIG, bool DROP, bool SPARSE, bool WITH_D>
-__global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BwdArgs a) {
-  using Cfg = DqCfg<D>;
+__global__ __launch_bounds__((DqCfg<D, SPARSE ? 128 : 256>::NT)) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BwdArgs a) {
+  using Cfg = DqCfg<D, SPARSE ? 128 : 256>;
   using vec8 = typename TR::vec8;
   constexpr int BQ = Cfg::BQ, BK = Cfg::BK, NT = Cfg::NT, CPR = Cfg::CPR, LPT = Cfg::LPT;
   constexpr int TILE_B = Cfg::TILE_B;
@@ -622,18 +621,21 @@ __global__ __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  // The work-group's 256 queries are two mask rows (waves 0-3 the first, 4-7 the second); key
-  // tile j lies in mask column j / TPC. The work-group visits the tiles whose column is set in
-  // either row, each wave computes those its own row allows; both rows are scanned 64 columns at
-  // a time (MaskLine), only right after the vmcnt wait that empties the prefetch queue.
-  static_assert(BQ == 256 && 128 % BK == 0, "a dQ work-group is two mask rows");
+  // Key tile j lies in mask column j / TPC. A work-group of 256 queries covers two mask rows
+  // (waves 0-3 the first, 4-7 the second): it visits the tiles whose column is set in either row,
+  // and each wave computes those its own row allows. The block-sparse instances use 128-query
+  // work-groups, one mask row, so no wave idles on a tile loaded for the other row. Rows are
+  // scanned 64 columns at a time (MaskLine), only right after the vmcnt wait that empties the
+  // prefetch queue.
+  static_assert((BQ == 256 || BQ == 128) && 128 % BK == 0, "a dQ work-group is one or two mask rows");
   constexpr int TPC = 128 / BK;  // key tiles per mask column
   const int r_lo = q_base >> 7;
   const uint8_t* bm = SPARSE ? a.bmask + (size_t)bh * a.nb * a.nb : nullptr;
   MaskLine row0 = mask_line(SPARSE ? bm + (size_t)r_lo * a.nb : nullptr, 1, SPARSE ? a.nb : 0);
-  MaskLine row1 = mask_line(SPARSE && r_lo + 1 < a.nb ? bm + (size_t)(r_lo + 1) * a.nb : nullptr, 1,
-                            SPARSE && r_lo + 1 < a.nb ? a.nb : 0);
-  const bool second_row = w >= 4;
+  constexpr bool kTwoRows = BQ == 256;
+  MaskLine row1 = mask_line(SPARSE && kTwoRows && r_lo + 1 < a.nb ? bm + (size_t)(r_lo + 1) * a.nb : nullptr, 1,
+                            SPARSE && kTwoRows && r_lo + 1 < a.nb ? a.nb : 0);
+  const bool second_row = kTwoRows && w >= 4;
   bool wave_on = true, wave_on_next = true;  // this wave's row allows the current / next tile
   auto next = [&](int j) {
     const int jj = j + 1;
@@ -777,10 +779,11 @@ hipError_t launch_all(const BwdReq& r, hipStream_t st, int stage) {
   };
   auto dq = [&](auto with_d) {
     constexpr bool WD = decltype(with_d)::value;
-    a.ntiles = (r.N + DqCfg<D>::BQ - 1) / DqCfg<D>::BQ;
+    using DC = DqCfg<D, SPARSE ? 128 : 256>;
+    a.ntiles = (r.N + DC::BQ - 1) / DC::BQ;
     a.hgroup = head_group(a.bh_total, (size_t)2 * r.N * D * 2);
     dim3 g2((unsigned)(BH * a.ntiles));
-    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, g2, dim3(DqCfg<D>::NT), 0, st, a); };
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, g2, dim3(DC::NT), 0, st, a); };
     if (r.causal)
       big ? go(bwd_dq_kernel<TR, D, true, true, DROP, SPARSE, WD>) : go(bwd_dq_kernel<TR, D, true, false, DROP, SPARSE, WD>);
     else
