@@ -333,6 +333,45 @@ def write_one_wave(run_dir, prof_dir):
                     "kernels read 2-5% high."))
 
 
+# The vendor's bf16 GEMM (torch.mm, which on ROCm runs a hipBLASLt kernel) on 8192^3, for the
+# clock and MFMA-busy fraction an MFMA-bound kernel without any softmax work reaches on this GPU.
+GEMM_N = 8192
+GEMM_KERNELS = (("hipBLASLt bf16 GEMM 8192 x 8192 x 8192", "Cijk_Ailk_Bljk_BBS", GEMM_N * GEMM_N // 1024,
+                 2.0 * GEMM_N ** 3),)
+GEMM_COMMANDS = {
+    key: "rocprofv3 --pmc " + ctrs + " --output-format csv -d {run}/" + key + " -o run -- "
+         f"python -u io_aware_tiled_fattn_amd/microbench/gemm_ceiling.py --sizes {GEMM_N}"
+    for key, ctrs in STALL_COUNTERS.items()
+}
+
+
+def write_gemm(run_dir, prof_dir, times_path=None):
+    """Counter summary of the library GEMM (GEMM_KERNELS), plus the timed sizes of
+    gemm_ceiling.py when its JSON lines are given."""
+    name = "gemm_ceiling_bf16_hipblaslt.md"
+    rows = write_stalls(
+        run_dir, prof_dir, kernels=GEMM_KERNELS, commands=GEMM_COMMANDS,
+        title="The vendor's bf16 GEMM on the same GPU: a practical ceiling for MFMA-bound kernels",
+        runs_note=("Every figure is the mean over the GEMM kernel's launches in the pass (gemm_ceiling.py "
+                   f"--sizes {GEMM_N}: a second of untimed calls, then five blocks of 20 timed ones, all counted). "
+                   "torch.mm on ROCm runs a hipBLASLt (Tensile) kernel; the row is matched by its name "
+                   "prefix and grid."),
+        name=name,
+        clock_note=("The counter also runs through each dispatch's own set-up (some 18 to 28 thousand "
+                    "cycles, measured on the attention kernels' passes), so the clock of this 760 us "
+                    "kernel reads about 1% high."))
+    if times_path:
+        res = [json.loads(x) for x in open(times_path) if x.startswith("{")]
+        lines = ["", "Timed with HIP events (`python -u io_aware_tiled_fattn_amd/microbench/gemm_ceiling.py`, "
+                 "median of five blocks of 20 calls after a second of warm-up):", "",
+                 "| GEMM | ms per call | TFLOP/s | of the 2516.6 TFLOP/s nominal peak |", "|---|---|---|---|"]
+        for r in res:
+            lines.append(f"| {r['gemm']} | {r['ms']:.4f} | {r['tflops']:.1f} | {r['frac_of_peak']:.1%} |")
+        with open(os.path.join(prof_dir, name), "a") as f:
+            f.write("\n".join(lines) + "\n")
+    return rows
+
+
 def _is_decode(kernel):
     return any(kernel.startswith(d) for d in DECODE_KERNELS)
 
@@ -537,6 +576,10 @@ if __name__ == "__main__":
         sys.exit(0)
     if sys.argv[1] == "onewave":
         for r in write_one_wave(sys.argv[2], sys.argv[3]):
+            print(r)
+        sys.exit(0)
+    if sys.argv[1] == "gemm":
+        for r in write_gemm(sys.argv[2], sys.argv[3], sys.argv[4] if len(sys.argv) > 4 else None):
             print(r)
         sys.exit(0)
     if sys.argv[1] == "stalls":

@@ -133,3 +133,27 @@ def test_kernel_times_are_split_by_grid(tmp_path):
     rows = {r["grid"]: r for r in profiling.kernel_stats_by_grid(str(tmp_path))}
     assert rows[262144]["calls"] == 2 and abs(rows[262144]["avg_us"] - 0.2) < 1e-12
     assert rows[524288]["calls"] == 1 and abs(rows[524288]["pct"] - 1000 / 14) < 1e-9
+
+
+def test_gemm_summary_row_and_timings(tmp_path):
+    # one library GEMM launch of 800 us at 2000 MHz with the MFMA unit busy 70% of the SIMD cycles
+    ns, cyc = 800_000, 1_600_000
+    name = "Cijk_Ailk_Bljk_BBS_BH_MT256x256x64"
+    t = lambda did, c, v: {"Dispatch_Id": did, "Kernel_Name": name, "Grid_Size": 65536, "Counter_Name": c,
+                           "Counter_Value": v, "Start_Timestamp": 0, "End_Timestamp": ns}
+    sq1 = [t(1, c, 1.0) for c in ("SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                                  "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS")]
+    sq1.append(t(1, "GRBM_GUI_ACTIVE", 8.0 * cyc))
+    sq2 = [t(2, "SQ_VALU_MFMA_BUSY_CYCLES", 0.7 * 1024 * cyc), t(2, "SQ_VALU_MFMA_COEXEC_CYCLES", 0.0),
+           t(2, "SQ_INSTS_MFMA", 100.0), t(2, "SQ_INSTS_VALU", 150.0), t(2, "SQ_INSTS_LDS", 40.0),
+           t(2, "SQ_INSTS_SALU", 10.0), t(2, "SQ_LDS_BANK_CONFLICT", 0.0), t(2, "GRBM_GUI_ACTIVE", 8.0 * cyc)]
+    _write_timed(str(tmp_path / "sq1" / "run_counter_collection.csv"), sq1)
+    _write_timed(str(tmp_path / "sq2" / "run_counter_collection.csv"), sq2)
+    times = tmp_path / "time.jsonl"
+    times.write_text('noise\n{"gemm": "bf16 8192x8192x8192", "ms": 0.8, "tflops": 1374.4, "frac_of_peak": 0.5461}\n')
+    (r,) = profiling.write_gemm(str(tmp_path), str(tmp_path / "out"), str(times))
+    assert abs(r["mhz"] - 2000.0) < 1e-9 and abs(r["mfma_busy"] - 0.7) < 1e-12
+    assert abs(r["tflops"] - 2.0 * 8192 ** 3 / 8e-4 / 1e12) < 1e-6
+    assert abs(r["valu_per_mfma"] - 0.5) < 1e-12
+    text = (tmp_path / "out" / "gemm_ceiling_bf16_hipblaslt.md").read_text()
+    assert "| bf16 8192x8192x8192 | 0.8000 | 1374.4 | 54.6% |" in text
