@@ -214,18 +214,6 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
   const int key = key0 + lr;              // this lane's key
   const bool wave_active = key0 < N;
 
-  // MFMA B operand of the first product: K for A (S = Q K^T), V for B (dP = dO V^T);
-  // lane holds X[key][16s + 8h .. +7].
-  vec8 xf[D / 16];
-  {
-    const uint16_t* src = (role_a ? a.k : a.v) + head;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      u32x4 r = {0u, 0u, 0u, 0u};
-      if (key < N) r = *(const u32x4*)(src + (size_t)key * D + 16 * s + 8 * h);
-      xf[s] = bitcast<vec8>(r);
-    }
-  }
   f32x16 acc[D / 32];  // dV (A) or dK (B)
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
@@ -287,14 +275,14 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
   auto load_rows = [&](int i) {
     if (tid < BQ) {
       const int q = min(i * BQ + tid, N - 1);
-      lr2 = a.lse[rowbase + q] * kLog2e;
+      lr2 = a.lse[rowbase + q];  // scaled to log2 units when stored, so the load need not land first
       dvr = a.dvec[rowbase + q];
     }
   };
   auto store_rows = [&](int p) {
     if (tid < BQ) {
       float* rows = (float*)(stage(p) + 2 * TILE_B);
-      rows[tid] = lr2;
+      rows[tid] = lr2 * kLog2e;
       rows[BQ + tid] = dvr;
     }
   };
@@ -323,8 +311,21 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
   if (cur < n_qt) {
     load_rows(cur);
     issue(cur, 0);
-    store_rows(0);
   }
+  // MFMA B operand of the first product: K for A (S = Q K^T), V for B (dP = dO V^T);
+  // lane holds X[key][16s + 8h .. +7] (zeros past the last key; the loads themselves read key
+  // N - 1, so they need no branch). The first query tile's loads are already in flight.
+  vec8 xf[D / 16];
+  {
+    const uint16_t* src = (role_a ? a.k : a.v) + head + (size_t)min(key, N - 1) * D;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 r = *(const u32x4*)(src + 16 * s + 8 * h);
+      if (key >= N) r = u32x4{0u, 0u, 0u, 0u};
+      xf[s] = bitcast<vec8>(r);
+    }
+  }
+  if (cur < n_qt) store_rows(0);
   // iteration p: A runs the tile at position p, B the one at p - 1; the last iteration is B's.
   // A dense run counts p over the tile indices i_begin .. n_qt.
   for (int p = 0; cur < n_qt || prev >= 0; ++p) {
@@ -526,40 +527,6 @@ __global__ __launch_bounds__((DqCfg<D, SPARSE ? 128 : 256>::NT)) __attribute__((
   const bool wave_active = q0 < N;
   const int wave_kv_end = CAUSAL ? min(q0 + 31, N - 1) + 1 : N;
 
-  // Q^T and dO^T fragments as MFMA B operands: lane holds X[qrow][16s + 8h .. +7].
-  vec8 qf[D / 16], df[D / 16];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    u32x4 qr = {0u, 0u, 0u, 0u}, dr = {0u, 0u, 0u, 0u};
-    if (qrow < N) {
-      qr = *(const u32x4*)(a.q + head + (size_t)qrow * D + 16 * s + 8 * h);
-      dr = *(const u32x4*)(a.dO + head + (size_t)qrow * D + 16 * s + 8 * h);
-    }
-    qf[s] = bitcast<vec8>(qr);
-    df[s] = bitcast<vec8>(dr);
-  }
-  const float lse2 = qrow < N ? a.lse[(size_t)bh * N + qrow] * kLog2e : __builtin_inff();
-  float dval;
-  if constexpr (WITH_D) {
-    // lane (h, lr) holds chunks p = 2s + h of its row; the preprocess tree pairs chunk p with
-    // p ^ D/16, then p ^ D/32, ..., within the lane, and finally p ^ 1 across the two halves
-    float ps[D / 16];
-#pragma unroll
-    for (int s2 = 0; s2 < D / 16; ++s2) {
-      u32x4 orw = {0u, 0u, 0u, 0u};
-      if (qrow < N) orw = *(const u32x4*)(a.o + head + (size_t)qrow * D + 16 * s2 + 8 * h);
-      ps[s2] = chunk_dot<TR>(orw, bitcast<u32x4>(df[s2]));
-    }
-#pragma unroll
-    for (int off = D / 32; off >= 1; off >>= 1)
-#pragma unroll
-      for (int s2 = 0; s2 < off; ++s2) ps[s2] = ps[s2] + ps[s2 + off];
-    dval = sum_halves(ps[0]);
-    if (qrow < N && h == 0) a.dvec[(size_t)bh * N + qrow] = dval;
-  } else {
-    dval = qrow < N ? a.dvec[(size_t)bh * N + qrow] : 0.f;
-  }
-
   f32x16 acc[D / 32];
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
@@ -650,6 +617,45 @@ __global__ __launch_bounds__((DqCfg<D, SPARSE ? 128 : 256>::NT)) __attribute__((
   int j = next(-1);
   wave_on = wave_on_next;
   if (j < n_kv) issue(j, 0);
+
+  // The first key tile's loads are in flight while the wave reads its Q, dO (and O) rows.
+  // Q^T and dO^T fragments as MFMA B operands: lane holds X[qrow][16s + 8h .. +7].
+  // (zeros past the last row; the loads themselves read row N - 1, so they need no branch)
+  const int qsrc = min(qrow, N - 1);
+  u32x4 qr[D / 16], dr[D / 16], orw[WITH_D ? D / 16 : 1];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    qr[s] = *(const u32x4*)(a.q + head + (size_t)qsrc * D + 16 * s + 8 * h);
+    dr[s] = *(const u32x4*)(a.dO + head + (size_t)qsrc * D + 16 * s + 8 * h);
+    if constexpr (WITH_D) orw[s] = *(const u32x4*)(a.o + head + (size_t)qsrc * D + 16 * s + 8 * h);
+  }
+  const float lse_row = a.lse[(size_t)bh * N + qsrc];
+  const float d_row = WITH_D ? 0.f : a.dvec[(size_t)bh * N + qsrc];
+  // every row load is issued before the first one is used, so their latencies overlap
+  __builtin_amdgcn_sched_barrier(0);
+  vec8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    if (qrow >= N) qr[s] = dr[s] = u32x4{0u, 0u, 0u, 0u};
+    qf[s] = bitcast<vec8>(qr[s]);
+    df[s] = bitcast<vec8>(dr[s]);
+  }
+  const float lse2 = qrow < N ? lse_row * kLog2e : __builtin_inff();
+  float dval = qrow < N ? d_row : 0.f;
+  if constexpr (WITH_D) {
+    // lane (h, lr) holds chunks p = 2s + h of its row; the preprocess tree pairs chunk p with
+    // p ^ D/16, then p ^ D/32, ..., within the lane, and finally p ^ 1 across the two halves
+    float ps[D / 16];
+#pragma unroll
+    for (int s2 = 0; s2 < D / 16; ++s2) ps[s2] = chunk_dot<TR>(orw[s2], bitcast<u32x4>(df[s2]));
+#pragma unroll
+    for (int off = D / 32; off >= 1; off >>= 1)
+#pragma unroll
+      for (int s2 = 0; s2 < off; ++s2) ps[s2] = ps[s2] + ps[s2 + off];
+    dval = qrow < N ? sum_halves(ps[0]) : 0.f;
+    if (qrow < N && h == 0) a.dvec[(size_t)bh * N + qrow] = dval;
+  }
+
   for (int t = 0; j < n_kv; ++t) {
     wait_vmcnt<0>();
     barrier_lds();

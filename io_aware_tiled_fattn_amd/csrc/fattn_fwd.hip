@@ -136,16 +136,6 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   const int wave_last = min(q0 + 31, N - 1);
   const int wave_kv_end = CAUSAL ? wave_last + 1 : N;
 
-  // Q^T fragments: lane holds Q[qrow][16s + 8h .. +7].
-  vec8 qf[D / 16];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (qrow < N) raw = *(const u32x4*)(Qh + (size_t)qrow * D + 16 * s + 8 * h);
-    raw = (raw ^ a.neg_mask) & a.keep_mask;
-    qf[s] = bitcast<vec8>(raw);
-  }
-
   const int kv_end = CAUSAL ? min(N, q_base + BR) : N;
   const int n_kv = (kv_end + BC - 1) / BC;
 
@@ -199,6 +189,20 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
       }
     }
   };
+  // The first tiles' loads go out before the Q rows are read, so the two latencies overlap.
+  if (!SPARSE)
+    for (int t = 0; t < NS - 1 && t < n_kv; ++t) issue(t, t);
+
+  // Q^T fragments: lane holds Q[qrow][16s + 8h .. +7] (zeros past the last row; the load itself
+  // reads row N - 1, so it needs no branch).
+  vec8 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    u32x4 raw = *(const u32x4*)(Qh + (size_t)min(qrow, N - 1) * D + 16 * s + 8 * h);
+    if (qrow >= N) raw = u32x4{0u, 0u, 0u, 0u};
+    raw = (raw ^ a.neg_mask) & a.keep_mask;
+    qf[s] = bitcast<vec8>(raw);
+  }
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -332,7 +336,6 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   f32x16 s[BC / 32];
   float m_new = 0.f;
   if constexpr (!SPARSE) {
-    for (int t = 0; t < NS - 1 && t < n_kv; ++t) issue(t, t);
     int j = 0;
     while (j < n_kv) {
       bool grew = false;
