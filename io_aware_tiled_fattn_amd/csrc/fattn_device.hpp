@@ -76,7 +76,11 @@ __device__ inline float sum_halves(float x) {
 // chunks addressed by lanes 4e + j / 4 (e = 0..3), i.e. a 4 x 16 block of 16-bit elements whose
 // four rows are addressed by lanes {0..3}, {4..7}, {8..11}, {12..15} (each lane one 4-element
 // quarter of its row) comes back column by column.
-__device__ inline i16x4 lds_read_tr16(const void* p) {
+// The pointer is declared restrict so that, once inlined, the read carries alias-scope
+// information: the compiler then does not make it wait for every global->LDS load in flight
+// (the kernels' own waits and barriers order those; a transposed read never touches a stage
+// that is still being filled).
+__device__ inline i16x4 lds_read_tr16(const void* __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 

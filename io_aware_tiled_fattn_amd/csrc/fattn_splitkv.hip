@@ -230,6 +230,11 @@ __global__ __launch_bounds__(64) void splitkv_kernel(SplitArgs a) {
         pf[2 * kb + half] = bitcast<vec8>(packed);
       }
     l_part += ls;
+    // The tiles still in flight land before the V^T reads; the next iterations' waits then find
+    // nothing outstanding, and each tile's loads overlap only the score phase that follows their
+    // issue. Measured on the decode workload (B=8 H=32 Nk=16384): 2.4% faster than keeping up to
+    // NS - 1 tiles in flight through the whole loop.
+    wait_vmcnt<0>();
 #pragma unroll
     for (int c = 0; c < BC / 16; ++c)
 #pragma unroll
