@@ -477,7 +477,7 @@ __global__ __launch_bounds__(PairCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(
 // ---------------------------------------------------------------------------------------------
 // 3. dQ.
 //
-// One work-group per (b*h, 256-query tile), the forward's layout: S^T = K Q^T and dP^T = V dO^T
+// One work-group per (b*h, 256-query tile; 128 queries in block-sparse runs), the forward's layout: S^T = K Q^T and dP^T = V dO^T
 // give each lane ONE query (its LSE and D are per-lane scalars); dQ^T += K^T dS^T takes K^T from
 // the K tile through the transposed read. K and V tiles of 64 keys stream memory -> LDS, two
 // stages deep.
@@ -588,34 +588,22 @@ __global__ __launch_bounds__((DqCfg<D, SPARSE ? 128 : 256>::NT)) __attribute__((
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  // Key tile j lies in mask column j / TPC. A work-group of 256 queries covers two mask rows
-  // (waves 0-3 the first, 4-7 the second): it visits the tiles whose column is set in either row,
-  // and each wave computes those its own row allows. The block-sparse instances use 128-query
-  // work-groups, one mask row, so no wave idles on a tile loaded for the other row. Rows are
-  // scanned 64 columns at a time (MaskLine), only right after the vmcnt wait that empties the
-  // prefetch queue.
-  static_assert((BQ == 256 || BQ == 128) && 128 % BK == 0, "a dQ work-group is one or two mask rows");
+  // Key tile j lies in mask column j / TPC. A block-sparse work-group holds 128 queries, one mask
+  // row, and visits only the key tiles that row allows; the row is scanned 64 columns at a time
+  // (MaskLine), only right after the vmcnt wait that empties the prefetch queue.
+  static_assert(!SPARSE || (BQ == 128 && 128 % BK == 0), "a block-sparse dQ work-group is one mask row");
   constexpr int TPC = 128 / BK;  // key tiles per mask column
-  const int r_lo = q_base >> 7;
-  const uint8_t* bm = SPARSE ? a.bmask + (size_t)bh * a.nb * a.nb : nullptr;
-  MaskLine row0 = mask_line(SPARSE ? bm + (size_t)r_lo * a.nb : nullptr, 1, SPARSE ? a.nb : 0);
-  constexpr bool kTwoRows = BQ == 256;
-  MaskLine row1 = mask_line(SPARSE && kTwoRows && r_lo + 1 < a.nb ? bm + (size_t)(r_lo + 1) * a.nb : nullptr, 1,
-                            SPARSE && kTwoRows && r_lo + 1 < a.nb ? a.nb : 0);
-  const bool second_row = kTwoRows && w >= 4;
-  bool wave_on = true, wave_on_next = true;  // this wave's row allows the current / next tile
+  MaskLine mrow = mask_line(SPARSE ? a.bmask + ((size_t)bh * a.nb + (q_base >> 7)) * a.nb : nullptr, 1,
+                            SPARSE ? a.nb : 0);
   auto next = [&](int j) {
     const int jj = j + 1;
     if (!SPARSE) return jj;
     if (jj >= n_kv) return n_kv;
-    if (jj % TPC != 0) return jj;  // the same column: the wave's flag carries over
-    const int c0 = mask_next(row0, jj / TPC, lane), c1 = mask_next(row1, jj / TPC, lane);
-    const int c = min(c0, c1);
-    wave_on_next = (second_row ? c1 : c0) == c;
+    if (jj % TPC != 0) return jj;  // the same mask column
+    const int c = mask_next(mrow, jj / TPC, lane);
     return c >= (n_kv + TPC - 1) / TPC ? n_kv : c * TPC;
   };
   int j = next(-1);
-  wave_on = wave_on_next;
   if (j < n_kv) issue(j, 0);
 
   // The first key tile's loads are in flight while the wave reads its Q, dO (and O) rows.
@@ -662,11 +650,8 @@ __global__ __launch_bounds__((DqCfg<D, SPARSE ? 128 : 256>::NT)) __attribute__((
     const int jn = next(j);
     if (jn < n_kv) issue(jn, t + 1);
     const int k0 = j * BK;
-    const bool on = wave_on;
-    wave_on = wave_on_next;
     j = jn;
     if (!(wave_active && k0 < wave_kv_end)) continue;
-    if (SPARSE && !on) continue;
     const uint8_t* Ks = smem + (t & 1) * Cfg::STAGE_B;
     const uint8_t* Vs = Ks + TILE_B;
     const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > q0);
