@@ -19,9 +19,10 @@
 //               lane owns ONE key: P and dS then serve directly as the MFMA A operand of the
 //               second product, whose B operand (dO or Q with the query index as reduction
 //               index) comes from the same LDS tiles through ds_read_b64_tr_b16.
-//  3. bwd_dq:    one work-group per (b*h, 256-query tile), the forward's layout: S^T = K Q^T and
-//               dP^T = V dO^T give each lane ONE query (its LSE and D are per-lane scalars);
-//               dQ^T += K^T dS^T takes K^T from the row-major K tile via the transposed read.
+//  3. bwd_dq:    one work-group per (b*h, 256-query tile; 128 in block-sparse runs), the
+//               forward's layout: S^T = K Q^T and dP^T = V dO^T give each lane ONE query (its LSE
+//               and D are per-lane scalars); dQ^T += K^T dS^T takes K^T from the row-major K tile
+//               via the transposed read.
 // Every kernel writes its outputs once; there are no atomics, so results are deterministic.
 #include <type_traits>
 

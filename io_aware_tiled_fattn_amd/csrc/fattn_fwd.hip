@@ -9,8 +9,9 @@
 // visited (page 2, backward section and tips).
 //
 // gfx950 mapping (16-bit inputs):
-//  * a work-group of Br/32 waves; wave w owns query rows [q_base + 32w, +32). Two work-groups
-//    share a CU, so each SIMD runs two independent waves whose MFMA and VALU phases overlap.
+//  * a work-group of Br/32 waves; wave w owns query rows [q_base + 32w, +32). Each SIMD runs two
+//    waves whose MFMA and VALU phases can overlap: two of one 8-wave work-group for the 256-row
+//    tiles (d = 128), one of each of two 4-wave work-groups for the 128-row tiles.
 //  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: each lane then owns
 //    ONE query row (l % 32) and 16 keys per 32-key block, so the row max and row sum are
 //    in-register reductions plus one v_permlane32_swap between the two half-waves.

@@ -17,9 +17,9 @@
 // gfx950 mapping: one wave per work-group, its 32 query rows on the lanes exactly as in the
 // whole-row kernel (S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16, Q^T in registers, K read
 // from LDS with ds_read_b128, V with ds_read_b64_tr_b16). K/V tiles of BC keys go from memory
-// straight into LDS (buffer_load ... lds), NS stages deep, so NS - 1 tiles per wave are in flight
-// while one is computed. With one wave per work-group the LDS budget, not the register file,
-// sets how many tiles a CU keeps in flight; the kernel is bound by HBM bandwidth, and the MFMA
+// straight into LDS (buffer_load ... lds), NS stages deep: each tile's loads go out NS - 1 tiles
+// ahead of its use, and those still in flight are drained before a tile's V^T reads. With one
+// wave per work-group the LDS budget, not the register file, sets how far ahead a CU loads; the kernel is bound by HBM bandwidth, and the MFMA
 // work (32 query rows per tile even for one real query) stays far below its own bound.
 //
 // Causal with Nq queries and Nk keys: query i is position i + Nk - Nq of the sequence and sees
