@@ -88,7 +88,7 @@ __device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) 
 
 
 // ---- direct global -> LDS loads (buffer_load_dwordx4 ... lds) --------------------------------
-// One instruction moves 16 bytes per lane from memory straight into LDS, without VGRPs: lane i's
+// One instruction moves 16 bytes per lane from memory straight into LDS, without VGPRs: lane i's
 // 16 bytes land at LDS byte (lds + 16 * i), where lds is the same for the whole wave. The source
 // is the buffer resource's base + voffset (per lane) + soffset (scalar). Completion is tracked by
 // vmcnt; the caller waits with wait_vmcnt and then barriers before other waves read the data.
