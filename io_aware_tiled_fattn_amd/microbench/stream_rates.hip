@@ -8,8 +8,10 @@
 //              63 outstanding loads, so at most 3 tiles beyond the current one);
 //              the decode kernel's loads without its MFMA work. Tile orders: each work-group its own
 //              contiguous 2 MiB (the decode kernel's), grid-stride (tile t of work-group b is
-//              global tile t * 1024 + b), or 4-way interleave (4 work-groups share 8 MiB, member s
-//              takes tiles 4t + s).
+//              global tile t * 1024 + b), 4-way interleave (4 work-groups share 8 MiB, member s
+//              takes tiles 4t + s), or each work-group its own 2 MiB starting at a tile that
+//              depends on b and wrapping around (the same bytes per work-group, but work-groups
+//              that run together read at different offsets within their regions).
 //   vgpr:      16-byte global loads into registers, 1 or 4 waves per work-group, 2 or 4 tiles ahead.
 // Each variant: 5 warm-up launches, then the mean of 20 (HIP events).
 #include <hip/hip_runtime.h>
@@ -31,15 +33,18 @@ __global__ __launch_bounds__(64) void dma_ring(const uint8_t* src, uint32_t* out
   const int ntiles = REGION / TILE;
   // MODE 0: work-group b streams its own 2 MiB region; MODE 1: tile t of work-group b is global
   // tile t * nwg + b (grid-stride); MODE 2: groups of 4 work-groups share an 8 MiB region, tile t
-  // of member s is tile 4 t + s of the region
-  const uint8_t* base = MODE == 0 ? src + (size_t)blockIdx.x * REGION
+  // of member s is tile 4 t + s of the region; MODE 3 and 4: as MODE 0, but tile t of work-group b
+  // is tile (t + r) mod 128 of its region, with r = 37 b mod 128 (MODE 3) or r = b mod 128 (MODE 4)
+  const uint8_t* base = MODE == 0 || MODE >= 3 ? src + (size_t)blockIdx.x * REGION
                       : MODE == 1 ? src : src + (size_t)(blockIdx.x / 4) * 4 * REGION;
-  const uint32_t nrec = MODE == 1 ? 0xffffffffu : (uint32_t)(MODE == 0 ? REGION : 4 * REGION);
+  const uint32_t nrec = MODE == 1 ? 0xffffffffu : (uint32_t)(MODE == 2 ? 4 * REGION : REGION);
+  const int rot = MODE == 3 ? (int)((blockIdx.x * 37u) % (REGION / TILE)) : (int)(blockIdx.x % (REGION / TILE));
   const __amdgpu_buffer_rsrc_t r = make_rsrc(base, nrec);
   auto tile_off = [&](int t) -> size_t {
     return MODE == 0 ? (size_t)t * TILE
          : MODE == 1 ? ((size_t)t * gridDim.x + blockIdx.x) * TILE
-                     : ((size_t)t * 4 + (blockIdx.x & 3)) * TILE;
+         : MODE == 2 ? ((size_t)t * 4 + (blockIdx.x & 3)) * TILE
+                     : (size_t)((t + rot) % ntiles) * TILE;
   };
   auto issue = [&](int t) {
     uint8_t* st = smem + (t % NS) * TILE;
@@ -127,6 +132,9 @@ int main() {
   rc |= timeit("dma ring 1 wave, 5 stages", [&] { hipLaunchKernelGGL((dma_ring<5>), dim3(nwg), dim3(64), 0, 0, src, out); }, (double)total);
   rc |= timeit("dma ring 1 wave, 4 stages, grid-stride", [&] { hipLaunchKernelGGL((dma_ring<4, 1>), dim3(nwg), dim3(64), 0, 0, src, out); }, (double)total);
   rc |= timeit("dma ring 1 wave, 4 stages, 4-way interleave", [&] { hipLaunchKernelGGL((dma_ring<4, 2>), dim3(nwg), dim3(64), 0, 0, src, out); }, (double)total);
+  rc |= timeit("dma ring 1 wave, 4 stages, start 37b mod 128", [&] { hipLaunchKernelGGL((dma_ring<4, 3>), dim3(nwg), dim3(64), 0, 0, src, out); }, (double)total);
+  rc |= timeit("dma ring 1 wave, 4 stages, start b mod 128", [&] { hipLaunchKernelGGL((dma_ring<4, 4>), dim3(nwg), dim3(64), 0, 0, src, out); }, (double)total);
+  rc |= timeit("dma ring 1 wave, 4 stages (again)", [&] { hipLaunchKernelGGL((dma_ring<4>), dim3(nwg), dim3(64), 0, 0, src, out); }, (double)total);
   rc |= timeit("vgpr 1 wave, depth 2", [&] { hipLaunchKernelGGL((vgpr_stream<1, 2>), dim3(nwg), dim3(64), 0, 0, src, out); }, (double)total);
   rc |= timeit("vgpr 1 wave, depth 4", [&] { hipLaunchKernelGGL((vgpr_stream<1, 4>), dim3(nwg), dim3(64), 0, 0, src, out); }, (double)total);
   rc |= timeit("vgpr 4 waves, depth 2", [&] { hipLaunchKernelGGL((vgpr_stream<4, 2>), dim3(nwg), dim3(256), 0, 0, src, out); }, (double)total);
