@@ -122,6 +122,44 @@ __device__ inline void barrier_lds() {
   asm volatile("" ::: "memory");
 }
 
+// Store of a wave's 32 output rows of D 16-bit elements held the MFMA accumulator way (lane l owns
+// row l % 32 and, in vals[4b + g], the 4 elements at columns 32b + 8g + 4(l / 32) .. + 3 as two
+// packed pairs). Stored directly, each store instruction would write 8 bytes into each of 32 rows.
+// The rows go through `stage` (RP * D * 2 bytes of LDS that no other wave uses meanwhile; 16-byte
+// chunks XOR-swizzled per row), RP rows at a time, and leave as 16-byte stores that cover
+// 64 / (D / 8) whole rows per instruction. Rows r >= nvalid are not stored. `out` is row 0,
+// 16-byte aligned, rows D elements apart.
+template <int D, int RP>
+__device__ inline void store_rows_via_lds(const u32x2 (&vals)[D / 8], uint8_t* stage, uint16_t* out, int nvalid) {
+  static_assert(RP == 16 || RP == 32, "rows per pass");
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;  // rows per read instruction
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, h = lane >> 5;
+  const int cc = lane % CPR;
+#pragma unroll
+  for (int p = 0; p < 32 / RP; ++p) {
+    const int sr = lr - p * RP;  // this lane's row within the pass
+    if (sr >= 0 && sr < RP) {
+#pragma unroll
+      for (int c = 0; c < CPR; ++c)
+        *(u32x2*)(stage + sr * (D * 2) + ((c ^ (sr & (CPR - 1))) << 4) + 8 * h) = vals[c];
+    }
+    // the same wave reads what its other lanes wrote: LDS serves one wave's accesses in order,
+    // and the wait and the compiler barriers keep the reads after the writes (and the next
+    // pass's writes after these reads)
+    __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < RP / RPI; ++i) {
+      const int r = i * RPI + lane / CPR;
+      const u32x4 x = *(const u32x4*)(stage + r * (D * 2) + ((cc ^ (r & (CPR - 1))) << 4));
+      if (p * RP + r < nvalid) *(u32x4*)(out + (size_t)(p * RP + r) * D + cc * 8) = x;
+    }
+    asm volatile("" ::: "memory");
+  }
+}
+
 // XOR swizzles of the 16-byte chunks of a row-major LDS tile (rows of D 16-bit elements), chosen
 // so that the reads below hit distinct banks:
 //  * K tiles are read with ds_read_b128, 32 consecutive rows at one chunk column per instruction;

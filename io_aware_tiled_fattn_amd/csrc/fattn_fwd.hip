@@ -336,7 +336,9 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
   // all of it on every tile).
   f32x16 s[BC / 32];
   float m_new = 0.f;
+  int free_stage;  // an LDS stage that no wave reads or loads into once its loop has ended
   if constexpr (!SPARSE) {
+    free_stage = n_kv % NS;  // the last tile, n_kv - 1, sits in the stage before it
     int j = 0;
     while (j < n_kv) {
       bool grew = false;
@@ -416,24 +418,26 @@ __global__ __launch_bounds__(BR / 32 * 64) void fwd_kernel(FwdArgs a) {
       j = jn;
       ++t;
     }
+    free_stage = t % NS;  // positions 0 .. t - 1 were visited
   }
 
   if (!wave_active) return;
   const float l_tot = sum_halves(l_part);
-  if (qrow >= N) return;
   float inv = (DROP ? a.drop.inv_keep : 1.0f) / l_tot;
   if (SPARSE && !(l_tot > 0.f)) inv = 0.f;  // no allowed key: O = 0
-  uint16_t* Orow = a.o + head + (size_t)qrow * D;
+  u32x2 ov[D / 8];
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      u32x2 v2;
-      v2[0] = TR::pack2(acc[b][4 * jj] * inv, acc[b][4 * jj + 1] * inv);
-      v2[1] = TR::pack2(acc[b][4 * jj + 2] * inv, acc[b][4 * jj + 3] * inv);
-      *(u32x2*)(Orow + 32 * b + 8 * jj + 4 * h) = v2;
+      ov[4 * b + jj][0] = TR::pack2(acc[b][4 * jj] * inv, acc[b][4 * jj + 1] * inv);
+      ov[4 * b + jj][1] = TR::pack2(acc[b][4 * jj + 2] * inv, acc[b][4 * jj + 3] * inv);
     }
-  if (h == 0)
+  // O leaves through the free stage, each wave through its own slice of it
+  constexpr int RP = Cfg::STAGE_B >= Cfg::NW * 32 * D * 2 ? 32 : 16;
+  static_assert(Cfg::NW * RP * D * 2 <= Cfg::STAGE_B, "output staging");
+  store_rows_via_lds<D, RP>(ov, smem + free_stage * Cfg::STAGE_B + w * (RP * D * 2), a.o + head + (size_t)q0 * D, N - q0);
+  if (h == 0 && qrow < N)
     a.lse[(size_t)bh * N + qrow] = (SPARSE && !(l_tot > 0.f)) ? -__builtin_inff() : (m_ref + __log2f(l_tot)) * kLn2;
 }
 
