@@ -126,7 +126,9 @@ __device__ inline void barrier_lds() {
 // row l % 32 and, in vals[4b + g], the 4 elements at columns 32b + 8g + 4(l / 32) .. + 3 as two
 // packed pairs). Stored directly, each store instruction would write 8 bytes into each of 32 rows.
 // The rows go through `stage` (RP * D * 2 bytes of LDS that no other wave uses meanwhile; 16-byte
-// chunks XOR-swizzled per row), RP rows at a time, and leave as 16-byte stores that cover
+// chunks XOR-swizzled per row, and the two 8-byte halves of a chunk swapped in every other group
+// of D / 8 rows, so that the 8-byte writes of lanes l and l + D / 8 land in different banks), RP
+// rows at a time, and leave as 16-byte stores that cover
 // 64 / (D / 8) whole rows per instruction. Rows r >= nvalid are not stored. `out` is row 0,
 // 16-byte aligned, rows D elements apart.
 template <int D, int RP>
@@ -143,7 +145,7 @@ __device__ inline void store_rows_via_lds(const u32x2 (&vals)[D / 8], uint8_t* s
     if (sr >= 0 && sr < RP) {
 #pragma unroll
       for (int c = 0; c < CPR; ++c)
-        *(u32x2*)(stage + sr * (D * 2) + ((c ^ (sr & (CPR - 1))) << 4) + 8 * h) = vals[c];
+        *(u32x2*)(stage + sr * (D * 2) + ((c ^ (sr & (CPR - 1))) << 4) + 8 * (h ^ ((sr / CPR) & 1))) = vals[c];
     }
     // the same wave reads what its other lanes wrote: LDS serves one wave's accesses in order,
     // and the wait and the compiler barriers keep the reads after the writes (and the next
@@ -153,7 +155,8 @@ __device__ inline void store_rows_via_lds(const u32x2 (&vals)[D / 8], uint8_t* s
 #pragma unroll
     for (int i = 0; i < RP / RPI; ++i) {
       const int r = i * RPI + lane / CPR;
-      const u32x4 x = *(const u32x4*)(stage + r * (D * 2) + ((cc ^ (r & (CPR - 1))) << 4));
+      u32x4 x = *(const u32x4*)(stage + r * (D * 2) + ((cc ^ (r & (CPR - 1))) << 4));
+      if ((r / CPR) & 1) x = u32x4{x[2], x[3], x[0], x[1]};
       if (p * RP + r < nvalid) *(u32x4*)(out + (size_t)(p * RP + r) * D + cc * 8) = x;
     }
     asm volatile("" ::: "memory");
